@@ -1,0 +1,201 @@
+/*
+ * mok.h -- C ABI of libmok.so: one GPU's share of a deterministic
+ * Mixture-of-Experts layer step (forward and backward) on AMD MI355X (gfx950).
+ *
+ * The layer follows the Mixture-of-Kittens pages:
+ *  - "Cursor Mixture-of-Kittens cuts MoE training latency by 5.8x"
+ *    (dothoosh.com), section "Technical details of the MoK mechanism":
+ *    pull dispatch and push combine in the forward pass, pull reverse-combine
+ *    and push reverse-dispatch in the backward pass, all four driven by one
+ *    schedule table; BF16 and MXFP8; router-weight gradients fused into the
+ *    SwiGLU backward; grouped expert GEMMs sized for at least two full waves of
+ *    the machine; no token dropping.
+ *  - kwkr.cn MoK explainer, section 4.1 (top-k gating) and section 2
+ *    (determinism: the same inputs give the same bits).
+ *  - aikraft.ru MoK article, section 04 (pull dispatch; the CPU kept off the
+ *    critical path).
+ *
+ * On one GPU "dispatch" is a gather of token rows through the schedule's
+ * permutation straight into the GEMM's LDS tiles, and "combine" writes one
+ * partial row per (token, slot) that a second pass reduces in slot order.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - T tokens, hidden size H, E experts, top-k routing (k slots per token),
+ *    expert intermediate size I.  R = T*k routed rows.  Flat slot s = t*k + j.
+ *  - All arrays are row-major, device memory, 16-byte aligned, owned by the
+ *    caller.  The library never allocates, frees or synchronises; every call
+ *    only enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
+ *    and returns.  Nothing is read back to the host.
+ *  - Activation dtype `act` (MOK_F32 or MOK_BF16) is the storage type of
+ *    x, y, dy, dx, the router weight wr, the expert weights and every saved or
+ *    intermediate activation.  All arithmetic accumulates in fp32.
+ *  - Layouts: x, y, dy, dx [T][H]; wr [E][H]; w1 [E][2I][H] (rows 0..I-1 are
+ *    the SwiGLU gate projection, rows I..2I-1 the up projection); w2 [E][H][I];
+ *    idx [T][k] int32; gate, dgate, logits [T][k] / [T][E] fp32.
+ *  - Errors: arguments are checked before anything is enqueued and a status
+ *    is returned; nothing is thrown across the ABI.  A failed launch returns
+ *    MOK_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation of `stream`.
+ *  - Determinism: no floating-point atomics are used; every reduction runs in
+ *    a fixed order, so repeated calls with the same inputs and descriptor give
+ *    bit-identical outputs.
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mok_status {
+  MOK_OK = 0,
+  MOK_ERR_NULL = 1,  /* a required pointer is NULL */
+  MOK_ERR_ALIGN = 2, /* a pointer is not 16-byte aligned */
+  MOK_ERR_SHAPE = 3, /* a size in the descriptor is out of range (see mok_desc) */
+  MOK_ERR_DTYPE = 4, /* unsupported dtype combination */
+  MOK_ERR_HIP = 5    /* a HIP call (device query or kernel launch) failed */
+} mok_status;
+
+typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
+
+/* flags */
+#define MOK_FLAG_WGRAD_F32 1u /* dw1, dw2, dwr are written as fp32 instead of `act` */
+
+/*
+ * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;
+ * H and I positive multiples of 128; T*k < 2^31.  act is MOK_F32 or MOK_BF16
+ * and gemm must equal act (MOK_MXFP8 expert GEMMs are rejected with
+ * MOK_ERR_DTYPE by this version).
+ * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile
+ *   that still gives every grouped GEMM at least two full waves of the
+ *   GPU's compute units.
+ * grid: workgroups of the persistent GEMM kernels; 0 = one wave of the GPU.
+ * The same descriptor must be passed to mok_schedule_build and to the
+ * forward/backward calls that use that schedule.
+ */
+typedef struct mok_desc {
+  int64_t T;
+  int32_t H, E, k, I;
+  int32_t act;  /* mok_dtype */
+  int32_t gemm; /* mok_dtype */
+  uint32_t flags;
+  int32_t tile_m;
+  int32_t grid;
+  int32_t reserved;
+} mok_desc;
+
+/* Expert weights (device pointers, `act` dtype). */
+typedef struct mok_weights {
+  const void* w1; /* [E][2I][H] */
+  const void* w2; /* [E][H][I]  */
+} mok_weights;
+
+/* Sizes in bytes of the caller-owned buffers (worst case over routings). */
+typedef struct mok_sizes {
+  size_t sched;  /* schedule table (mok_schedule_build)                        */
+  size_t saved;  /* forward activations kept for the backward pass              */
+  size_t fwd_ws; /* forward scratch: per-(token,slot) partial rows [R][H]       */
+  size_t bwd_ws; /* backward scratch: dGU [R][2I], partials [R][H], d-gate parts */
+} mok_sizes;
+
+/* Byte offsets of the schedule table's parts inside the schedule buffer.
+ *   counts[E] int32            rows routed to each expert
+ *   offsets[E+1] int32         exclusive prefix sum of counts; offsets[E] = R
+ *   tile_start[E+1] int32      first tile of each expert; tile_start[E] = number of tiles
+ *   num_tiles int32            number of valid tiles (also tile_start[E])
+ *   perm[R] int32              routed row r -> flat slot t*k+j
+ *   inv[R] int32               flat slot -> routed row (inverse of perm)
+ *   tiles[max_tiles][4] int32  (expert, first routed row, rows <= tile_m, 0)
+ * Rows of one expert are contiguous and in ascending slot order (a stable
+ * sort of the slots by expert); tiles list experts in ascending order. */
+typedef struct mok_schedule_layout {
+  size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles;
+  int32_t tile_m;
+  int32_t max_tiles;
+} mok_schedule_layout;
+
+/* Layout of the `saved` buffer: au [R][2I] (fp32 accumulators a = x.W1_gate,
+ * u = x.W1_up rounded to `act`, routed-row order), then h [R][I]
+ * (h = silu(a)*u rounded to `act`).  au_offset/h_offset are byte offsets. */
+typedef struct mok_saved_layout {
+  size_t au_offset, h_offset;
+} mok_saved_layout;
+
+/* Fill *sizes for descriptor d.  Pure host computation. */
+mok_status mok_workspace_query(const mok_desc* d, mok_sizes* sizes);
+mok_status mok_schedule_layout_query(const mok_desc* d, mok_schedule_layout* layout);
+mok_status mok_saved_layout_query(const mok_desc* d, mok_saved_layout* layout);
+
+/*
+ * mok_route -- top-k router gating (kwkr.cn explainer, section 4.1).
+ *   z[t][e] = fp32 fused-multiply-add chain over h = 0..H-1 ascending of
+ *             x[t][h]*wr[e][h], starting from +0, then + bias[e] (one fp32 add).
+ *   idx[t][0..k-1]: the k largest z[t][.] -- larger first, equal values
+ *             (-0 == +0) ordered by lower expert index, NaN below everything.
+ *   gate[t][j] = exp(z_j - z_0) / sum_i exp(z_i - z_0)  (softmax over the k
+ *             selected logits, i.e. the full softmax renormalised over them).
+ * x [T][H] and wr [E][H] in `act`; bias [E] fp32 or NULL; idx [T][k] int32 and
+ * gate [T][k] fp32 are written; logits [T][E] fp32 is written when non-NULL.
+ */
+mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const float* bias, int32_t* idx,
+                     float* gate, float* logits, void* stream);
+
+/*
+ * mok_schedule_build -- the single schedule table shared by dispatch, combine,
+ * reverse-combine and reverse-dispatch (dothoosh.com page, "Technical details
+ * of the MoK mechanism").  A stable counting sort of the R flat slots by
+ * expert: counts, offsets, perm, inv, then the tile list.  Integer-exact and
+ * independent of launch order.  idx [T][k] int32 with values in [0, E)
+ * (values outside that range are a caller error and give an unspecified
+ * schedule); sched has mok_sizes.sched bytes.  The number of tiles stays on
+ * the device: the GEMM kernels read it there.
+ */
+mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched, void* stream);
+
+/*
+ * mok_moe_forward -- pull dispatch, grouped SwiGLU expert FFN, push combine.
+ * For every routed row r (slot s = perm[r] = t*k+j routed to expert e):
+ *   a = W1[e][0:I].x_t, u = W1[e][I:2I].x_t  (gathered straight into LDS),
+ *   h = silu(a)*u, o = W2[e].h  -> partial row s (rounded to `act`),
+ *   y_t = sum_{j=0..k-1} gate[t][j] * partial[t*k+j]   (fp32, slot order).
+ * Writes y [T][H], saved (mok_saved_layout), uses ws (mok_sizes.fwd_ws).
+ */
+mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, const float* gate,
+                           const mok_weights* w, void* y, void* saved, void* ws, void* stream);
+
+/*
+ * mok_moe_backward -- gradients of L = <dy, y>.
+ *   pull reverse-combine: dy rows gathered through perm into the dH GEMM;
+ *   dA = dy_t.W2[e]; the gate gradient g'_s = <dA, h> (= <dy_t, o_s>) is
+ *   formed in that GEMM's epilogue (SonicMoE-style fusion, dothoosh.com page,
+ *   "Technical details"), reduced over N-tiles in fixed order;
+ *   dh = g*dA; da = dh*u*sig(a)*(1 + a*(1 - sig(a))); du = dh*silu(a);
+ *   dGU = [da, du] (rounded to `act`); push reverse-dispatch:
+ *   q_s = dGU.W1[e] (rounded to `act`), dx_t = sum_j q_tj + sum_j dz_tj*wr[idx_tj];
+ *   dW1[e] = sum_r dGU_r x_t^T; dW2[e] = sum_r (g*dy_t rounded to act) h_r^T;
+ *   dz = g*(g' - sum_i g_i g'_i); dWr[e] = sum_{s routed to e} dz_s x_t.
+ * wr and dwr may both be NULL: the router backward is then skipped and dx
+ * holds only the expert term.  dgate [T][k] fp32 receives g'.  Every element
+ * of dw1 [E][2I][H], dw2 [E][H][I], dwr [E][H] is written (zero for experts
+ * without tokens).  ws has mok_sizes.bwd_ws bytes.
+ */
+mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x, const int32_t* idx,
+                            const float* gate, const mok_weights* w, const void* wr, const void* saved,
+                            const void* dy, void* dx, void* dw1, void* dw2, float* dgate, void* dwr, void* ws,
+                            void* stream);
+
+/* Static string naming a status code. */
+const char* mok_status_string(mok_status s);
+
+/* Library ABI version (major*100 + minor). */
+int32_t mok_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_H */
