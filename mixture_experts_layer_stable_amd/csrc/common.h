@@ -1,0 +1,81 @@
+// Shared device helpers for the gfx950 kernels of libmok.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/mok.h"
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+namespace mok {
+
+// bf16 values live in memory as uint16_t bit patterns.
+typedef uint16_t bf16;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Element traits: storage type T, elements per 16-byte vector, load/store of one element as float.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VE = 4;
+  static __device__ __forceinline__ float get(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void put(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16> {
+  static constexpr int VE = 8;
+  static __device__ __forceinline__ float get(const bf16* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void put(bf16* p, int64_t i, float v) { p[i] = (bf16)f32_to_bf16(v); }
+};
+
+// Unpack a 16-byte vector into floats / pack floats into one.
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[8], bf16*) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[4], float*) {
+  f[0] = __uint_as_float(v.x);
+  f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z);
+  f[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ uint4 pack(const float (&f)[8], bf16*) {
+  uint4 r;
+  r.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+  r.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  r.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
+  r.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
+  return r;
+}
+__device__ __forceinline__ uint4 pack(const float (&f)[4], float*) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void stg16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Logical workgroup index with consecutive indices on one XCD: the dispatcher
+// places workgroup b on XCD b % 8, so b -> (b % 8) * ceil(G/8) + b / 8 gives
+// each XCD a contiguous range (G need not be a multiple of 8).
+__device__ __forceinline__ int xcd_logical(int b, int G) {
+  const int per = (G + 7) / 8;
+  const int x = b % 8, i = b / 8;
+  const int full = G % 8 == 0 ? 8 : G % 8;  // XCDs that receive `per` workgroups
+  return x < full ? x * per + i : full * per + (x - full) * (per - 1) + i;
+}
+
+}  // namespace mok

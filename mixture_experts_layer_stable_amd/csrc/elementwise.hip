@@ -1,0 +1,168 @@
+// Bandwidth-bound kernels of the layer step, all with fixed summation orders.
+//
+//  combine     y_t = sum_{j=0..k-1} g_tj * partial[t*k+j]            (push combine)
+//  router_bwd  g'_tj = sum over dH N-tiles (ascending) of the d-gate partials;
+//              dz_tj = g_tj * (g'_tj - sum_i g_ti g'_ti)   (softmax over the top k)
+//  dx_reduce   dx_t = sum_j q[t*k+j] + sum_j dz_tj * wr[idx_tj]  (push reverse-dispatch)
+//  dwr         dWr[e] = sum over e's routed rows (ascending slot) of dz_s * x_t
+// Each thread owns one 16-byte vector of a row; loops over j / rows run in
+// ascending order with fp32 fused multiply-adds.
+#include "kernels.h"
+
+namespace mok {
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ part, const float* __restrict__ gate,
+                                                      T* __restrict__ y, int64_t T_, int H, int k) {
+  constexpr int VE = Elem<T>::VE;
+  const int vpr = H / VE;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= T_ * vpr) return;
+  const int64_t t = gid / vpr;
+  const int h0 = (int)(gid - t * vpr) * VE;
+  float acc[VE];
+#pragma unroll
+  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    const float g = gate[s];
+    float f[VE];
+    unpack(ldg16(part + s * H + h0), f, (T*)nullptr);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(g, f[q], acc[q]);
+  }
+  stg16(y + t * H + h0, pack(acc, (T*)nullptr));
+}
+
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgp, const float* __restrict__ gate,
+                                                         const int32_t* __restrict__ inv, float* __restrict__ dgate,
+                                                         float* __restrict__ dz, int64_t T_, int k, int R, int ntn) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T_) return;
+  float gp[16], g[16];
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t slot = t * k + j;
+    const int r = inv[slot];
+    float v = 0.0f;
+    for (int n = 0; n < ntn; ++n) v += dgp[(int64_t)n * R + r];
+    gp[j] = v;
+    g[j] = gate[slot];
+    s = __builtin_fmaf(g[j], v, s);
+  }
+  for (int j = 0; j < k; ++j) {
+    dgate[t * k + j] = gp[j];
+    dz[t * k + j] = g[j] * (gp[j] - s);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dx_reduce_kernel(const T* __restrict__ part, const float* __restrict__ dz,
+                                                        const int32_t* __restrict__ idx, const T* __restrict__ wr,
+                                                        T* __restrict__ dx, int64_t T_, int H, int k) {
+  constexpr int VE = Elem<T>::VE;
+  const int vpr = H / VE;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= T_ * vpr) return;
+  const int64_t t = gid / vpr;
+  const int h0 = (int)(gid - t * vpr) * VE;
+  float acc[VE];
+#pragma unroll
+  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float f[VE];
+    unpack(ldg16(part + (t * k + j) * H + h0), f, (T*)nullptr);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc[q] += f[q];
+  }
+  if (wr != nullptr) {
+    for (int j = 0; j < k; ++j) {
+      const float d = dz[t * k + j];
+      float f[VE];
+      unpack(ldg16(wr + (int64_t)idx[t * k + j] * H + h0), f, (T*)nullptr);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+    }
+  }
+  stg16(dx + t * H + h0, pack(acc, (T*)nullptr));
+}
+
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dz, const T* __restrict__ x,
+                                                  const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ perm, TO* __restrict__ dwr, int E, int H,
+                                                  int k) {
+  constexpr int VE = Elem<T>::VE;
+  const int vpr = H / VE;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)E * vpr) return;
+  const int e = (int)(gid / vpr);
+  const int h0 = (int)(gid - (int64_t)e * vpr) * VE;
+  float acc[VE];
+#pragma unroll
+  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
+  const int r1 = offsets[e + 1];
+  for (int r = offsets[e]; r < r1; ++r) {
+    const int s = perm[r];
+    const float d = dz[s];
+    float f[VE];
+    unpack(ldg16(x + (int64_t)(s / k) * H + h0), f, (T*)nullptr);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+  }
+  TO* o = dwr + (int64_t)e * H + h0;
+#pragma unroll
+  for (int q = 0; q < VE; ++q) Elem<TO>::put(o, q, acc[q]);
+}
+
+static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+hipError_t launch_combine(const Ctx& c, const void* part, const float* gate, void* y) {
+  if (c.T == 0) return hipSuccess;
+  if (c.act == MOK_F32) {
+    const int64_t n = c.T * (c.H / 4);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, c.s, (const float*)part, gate,
+                       (float*)y, c.T, c.H, c.k);
+  } else {
+    const int64_t n = c.T * (c.H / 8);
+    hipLaunchKernelGGL(combine_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, c.s, (const bf16*)part, gate,
+                       (bf16*)y, c.T, c.H, c.k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const Ctx& c, const float* dgp, const float* gate, float* dgate, float* dz) {
+  if (c.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(c.T)), dim3(256), 0, c.s, dgp, gate, c.inv, dgate, dz, c.T,
+                     c.k, c.R, dh_ntiles(c.I));
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_reduce(const Ctx& c, const void* part, const float* dz, const int32_t* idx, const void* wr,
+                            void* dx) {
+  if (c.T == 0) return hipSuccess;
+  if (c.act == MOK_F32) {
+    hipLaunchKernelGGL(dx_reduce_kernel<float>, dim3(blocks_for(c.T * (c.H / 4))), dim3(256), 0, c.s,
+                       (const float*)part, dz, idx, (const float*)wr, (float*)dx, c.T, c.H, c.k);
+  } else {
+    hipLaunchKernelGGL(dx_reduce_kernel<bf16>, dim3(blocks_for(c.T * (c.H / 8))), dim3(256), 0, c.s,
+                       (const bf16*)part, dz, idx, (const bf16*)wr, (bf16*)dx, c.T, c.H, c.k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr) {
+  if (c.act == MOK_F32) {
+    hipLaunchKernelGGL((dwr_kernel<float, float>), dim3(blocks_for((int64_t)c.E * (c.H / 4))), dim3(256), 0, c.s, dz,
+                       (const float*)x, c.offsets, c.perm, (float*)dwr, c.E, c.H, c.k);
+  } else if (c.wgrad_f32) {
+    hipLaunchKernelGGL((dwr_kernel<bf16, float>), dim3(blocks_for((int64_t)c.E * (c.H / 8))), dim3(256), 0, c.s, dz,
+                       (const bf16*)x, c.offsets, c.perm, (float*)dwr, c.E, c.H, c.k);
+  } else {
+    hipLaunchKernelGGL((dwr_kernel<bf16, bf16>), dim3(blocks_for((int64_t)c.E * (c.H / 8))), dim3(256), 0, c.s, dz,
+                       (const bf16*)x, c.offsets, c.perm, (bf16*)dwr, c.E, c.H, c.k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mok

@@ -1,0 +1,53 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+#include "common.h"
+
+namespace mok {
+
+// Everything a launch needs to know about the problem and the schedule.
+struct Ctx {
+  int64_t T;
+  int H, E, k, I;
+  int R;           // T*k routed rows
+  int act;         // MOK_F32 / MOK_BF16
+  bool wgrad_f32;  // weight gradients written as fp32
+  int BM;          // schedule tile rows
+  int max_tiles;
+  int num_cu;
+  int grid;        // persistent GEMM grid
+  hipStream_t s;
+  // schedule table (device)
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* tile_start;
+  int32_t* num_tiles;
+  int32_t* perm;
+  int32_t* inv;
+  int4* tiles;
+};
+
+hipError_t launch_route(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
+                        float* logits);
+hipError_t launch_schedule(const Ctx& c, const int32_t* idx);
+
+hipError_t launch_fc1(const Ctx& c, const void* x, const void* w1, void* au, void* h);
+hipError_t launch_fc2(const Ctx& c, const void* h, const void* w2, void* part);
+hipError_t launch_combine(const Ctx& c, const void* part, const float* gate, void* y);
+
+hipError_t launch_dh(const Ctx& c, const void* dy, const void* w2, const void* au, const void* h, const float* gate,
+                     void* dgu, float* dgp);
+hipError_t launch_router_bwd(const Ctx& c, const float* dgp, const float* gate, float* dgate, float* dz);
+hipError_t launch_dx(const Ctx& c, const void* dgu, const void* w1, void* part);
+hipError_t launch_dx_reduce(const Ctx& c, const void* part, const float* dz, const int32_t* idx, const void* wr,
+                            void* dx);
+hipError_t launch_dw2(const Ctx& c, const void* dy, const float* gate, const void* h, void* dw2);
+hipError_t launch_dw1(const Ctx& c, const void* dgu, const void* x, void* dw1);
+hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr);
+
+// Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
+inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }
+inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }
+// number of N-tiles of the dH GEMM (d-gate partials per routed row)
+inline int dh_ntiles(int I) { return I / bn_rows(I); }
+
+}  // namespace mok

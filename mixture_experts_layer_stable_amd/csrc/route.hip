@@ -1,0 +1,202 @@
+// Router: logits, top-k selection and gates in one kernel.
+//
+// Top-k gating (kwkr.cn MoK explainer, section 4.1). The routing decision is an
+// integer result that has to be reproducible bit for bit, so the logit of each
+// (token, expert) is a fixed-order fp32 fused-multiply-add chain over h
+// ascending, computed on the vector ALU (an MFMA would sum in an unspecified
+// internal order). Independent chains are interleaved across registers and
+// lanes; no single chain is reordered.
+//
+// Workgroup: 256 threads = 4 waves; TT = 4*TPT tokens; all E experts.
+// Lane l of wave w owns tokens w*TPT .. w*TPT+TPT-1 and experts l + 64*q,
+// q < EPT, so after the H loop every wave holds complete logit rows for its
+// tokens and selects the top k with butterfly shuffles (no LDS round trip).
+#include "kernels.h"
+
+namespace mok {
+
+constexpr int kRouteHC = 16;  // h values per LDS chunk
+constexpr int kNoExpert = 0x7FFFFFFF;
+
+// Strict total order of candidates: larger value first; equal values
+// (-0 == +0) by lower expert; NaN below every number; "no candidate" last.
+__device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
+  if (eb == kNoExpert) return ea != kNoExpert;
+  if (ea == kNoExpert) return false;
+  const bool na = a != a, nb = b != b;
+  if (na || nb) return (!na && nb) || (na && nb && ea < eb);
+  return a > b || (a == b && ea < eb);
+}
+
+template <typename T, int TPT, int EPT>
+__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, const T* __restrict__ wr,
+                                                    const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                    float* __restrict__ gate, float* __restrict__ logits, int64_t Tn,
+                                                    int H, int E, int k) {
+  constexpr int TT = 4 * TPT;
+  constexpr int EC = 64 * EPT;
+  constexpr int VE = Elem<T>::VE;
+  constexpr int VPR = kRouteHC / VE;  // 16-byte vectors per row chunk
+  __shared__ float sx[TT][kRouteHC];
+  __shared__ float sw[kRouteHC][EC];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+
+  float acc[TPT][EPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) acc[i][q] = 0.0f;
+
+  for (int h0 = 0; h0 < H; h0 += kRouteHC) {
+    for (int i = tid; i < TT * VPR; i += 256) {
+      const int t = i / VPR, vv = i % VPR;
+      const int64_t tok = t0 + t;
+      float f[VE];
+      if (tok < Tn) {
+        unpack(ldg16(x + tok * H + h0 + vv * VE), f, (T*)nullptr);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VE; ++q) f[q] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < VE; ++q) sx[t][vv * VE + q] = f[q];
+    }
+    for (int i = tid; i < EC * VPR; i += 256) {
+      const int e = i / VPR, vv = i % VPR;
+      float f[VE];
+      if (e < E) {
+        unpack(ldg16(wr + (int64_t)e * H + h0 + vv * VE), f, (T*)nullptr);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VE; ++q) f[q] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < VE; ++q) sw[vv * VE + q][e] = f[q];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int hh = 0; hh < kRouteHC; ++hh) {
+      float xv[TPT], wv[EPT];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) xv[i] = sx[wave * TPT + i][hh];
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) wv[q] = sw[hh][lane + 64 * q];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) acc[i][q] = __builtin_fmaf(xv[i], wv[q], acc[i][q]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll 1
+  for (int i = 0; i < TPT; ++i) {
+    const int64_t tok = t0 + wave * TPT + i;
+    if (tok >= Tn) break;
+    float v[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = acc[i][q];
+      if (bias != nullptr && e < E) v[q] = v[q] + bias[e];
+      if (logits != nullptr && e < E) logits[tok * E + e] = v[q];
+    }
+    uint32_t taken = 0;
+    float zsel[16];
+    int esel[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        float bv = 0.0f;
+        int be = kNoExpert;
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+          const int e = lane + 64 * q;
+          if (e < E && !((taken >> q) & 1u) && better(v[q], e, bv, be)) {
+            bv = v[q];
+            be = e;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int oe = __shfl_xor(be, off);
+          if (better(ov, oe, bv, be)) {
+            bv = ov;
+            be = oe;
+          }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        zsel[j] = bv;
+        esel[j] = be;
+      }
+    }
+    // softmax over the selected logits, summed in slot order
+    float ex[16];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        ex[j] = expf(zsel[j] - zsel[0]);
+        s = s + ex[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k && lane == j) {
+        idx[tok * k + j] = esel[j];
+        gate[tok * k + j] = ex[j] / s;
+      }
+    }
+  }
+}
+
+template <typename T, int TPT, int EPT>
+static hipError_t launch_route_t(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx,
+                                 float* gate, float* logits) {
+  const int64_t blocks = (c.T + 4 * TPT - 1) / (4 * TPT);
+  hipLaunchKernelGGL((route_kernel<T, TPT, EPT>), dim3((unsigned)blocks), dim3(256), 0, c.s, (const T*)x,
+                     (const T*)wr, bias, idx, gate, logits, c.T, c.H, c.E, c.k);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t route_dispatch(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx,
+                                 float* gate, float* logits) {
+  const int ept = (c.E + 63) / 64;
+  switch (ept) {
+#define MOK_ROUTE_CASE(N, TPT) \
+  case N:                      \
+    return launch_route_t<T, TPT, N>(c, x, wr, bias, idx, gate, logits);
+    MOK_ROUTE_CASE(1, 8)
+    MOK_ROUTE_CASE(2, 8)
+    MOK_ROUTE_CASE(3, 8)
+    MOK_ROUTE_CASE(4, 8)
+    MOK_ROUTE_CASE(5, 8)
+    MOK_ROUTE_CASE(6, 8)
+    MOK_ROUTE_CASE(7, 8)
+    MOK_ROUTE_CASE(8, 8)
+    MOK_ROUTE_CASE(9, 4)
+    MOK_ROUTE_CASE(10, 4)
+    MOK_ROUTE_CASE(11, 4)
+    MOK_ROUTE_CASE(12, 4)
+    MOK_ROUTE_CASE(13, 4)
+    MOK_ROUTE_CASE(14, 4)
+    MOK_ROUTE_CASE(15, 4)
+    MOK_ROUTE_CASE(16, 4)
+#undef MOK_ROUTE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_route(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
+                        float* logits) {
+  if (c.T == 0) return hipSuccess;
+  return c.act == MOK_F32 ? route_dispatch<float>(c, x, wr, bias, idx, gate, logits)
+                          : route_dispatch<bf16>(c, x, wr, bias, idx, gate, logits);
+}
+
+}  // namespace mok

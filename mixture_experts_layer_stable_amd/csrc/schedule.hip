@@ -1,0 +1,128 @@
+// The single schedule table (dothoosh.com MoK page, "Technical details of the
+// MoK mechanism": one schedule drives dispatch, combine, reverse-combine and
+// reverse-dispatch).
+//
+// A stable counting sort of the R = T*k flat slots by expert, done without
+// atomics so that it is exact and independent of scheduling:
+//   1. count:  one wave per expert scans idx and counts its slots;
+//   2. scan:   one workgroup forms exclusive offsets and per-expert tile starts
+//              and writes the tile list (expert, first row, rows);
+//   3. rank:   one wave per expert scans idx again in ascending slot order; a
+//              slot's row is offsets[e] + number of earlier slots of e
+//              (ballot + popcount), giving perm (row -> slot) and inv.
+#include "kernels.h"
+
+namespace mok {
+
+__global__ __launch_bounds__(64) void sched_count_kernel(const int32_t* __restrict__ idx, int R,
+                                                         int32_t* __restrict__ counts) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int n4 = R >> 2;
+  const int4* v4 = reinterpret_cast<const int4*>(idx);
+  int cnt = 0;
+  for (int i = lane; i < n4; i += 64) {
+    const int4 q = v4[i];
+    cnt += (q.x == e) + (q.y == e) + (q.z == e) + (q.w == e);
+  }
+  for (int i = (n4 << 2) + lane; i < R; i += 64) cnt += idx[i] == e;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if (lane == 0) counts[e] = cnt;
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// exclusive prefix and writes the total to *total.
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = s_wave[w];
+      s_wave[w] = acc;
+      acc += t;
+    }
+    s_wave[nw] = acc;
+  }
+  __syncthreads();
+  const int ex = s_wave[wave] + inc - v;
+  *total = s_wave[nw];
+  __syncthreads();
+  return ex;
+}
+
+__global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restrict__ counts, int E, int R, int BM,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ tile_start,
+                                                          int32_t* __restrict__ num_tiles, int4* __restrict__ tiles) {
+  __shared__ int s_wave[17];
+  const int e = threadIdx.x;
+  const int c = e < E ? counts[e] : 0;
+  const int nt = (c + BM - 1) / BM;
+  int tot_c, tot_t;
+  const int off = block_exclusive_scan(c, s_wave, &tot_c);
+  const int ts = block_exclusive_scan(nt, s_wave, &tot_t);
+  if (e < E) {
+    offsets[e] = off;
+    tile_start[e] = ts;
+    for (int m = 0; m < nt; ++m) tiles[ts + m] = make_int4(e, off + m * BM, min(BM, c - m * BM), 0);
+  }
+  if (e == 0) {
+    offsets[E] = R;
+    tile_start[E] = tot_t;
+    *num_tiles = tot_t;
+  }
+}
+
+__global__ __launch_bounds__(64) void sched_rank_kernel(const int32_t* __restrict__ idx, int R,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int base = offsets[e];
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int n4 = R >> 2;
+  const int4* v4 = reinterpret_cast<const int4*>(idx);
+  int running = 0;
+  for (int i0 = 0; i0 < n4; i0 += 64) {
+    const int i = i0 + lane;
+    int4 q = make_int4(-1, -1, -1, -1);
+    if (i < n4) q = v4[i];
+    const bool m0 = q.x == e, m1 = q.y == e, m2 = q.z == e, m3 = q.w == e;
+    const uint64_t b0 = __ballot(m0), b1 = __ballot(m1), b2 = __ballot(m2), b3 = __ballot(m3);
+    int r = running + __popcll(b0 & lt) + __popcll(b1 & lt) + __popcll(b2 & lt) + __popcll(b3 & lt);
+    const int s = i << 2;
+    if (m0) { perm[base + r] = s;     inv[s] = base + r;     ++r; }
+    if (m1) { perm[base + r] = s + 1; inv[s + 1] = base + r; ++r; }
+    if (m2) { perm[base + r] = s + 2; inv[s + 2] = base + r; ++r; }
+    if (m3) { perm[base + r] = s + 3; inv[s + 3] = base + r; }
+    running += __popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3);
+  }
+  for (int i0 = n4 << 2; i0 < R; i0 += 64) {
+    const int s = i0 + lane;
+    const bool m = s < R && idx[s] == e;
+    const uint64_t b = __ballot(m);
+    if (m) {
+      const int r = running + __popcll(b & lt);
+      perm[base + r] = s;
+      inv[s] = base + r;
+    }
+    running += __popcll(b);
+  }
+}
+
+hipError_t launch_schedule(const Ctx& c, const int32_t* idx) {
+  hipLaunchKernelGGL(sched_count_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.counts);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, c.s, c.counts, c.E, c.R, c.BM, c.offsets,
+                     c.tile_start, c.num_tiles, c.tiles);
+  if (c.R > 0) hipLaunchKernelGGL(sched_rank_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.offsets, c.perm, c.inv);
+  return hipGetLastError();
+}
+
+}  // namespace mok

@@ -1,0 +1,235 @@
+"""Thin Python binding of libmok.so (include/mok.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. Tensors are passed as device pointers (``tensor.data_ptr()``) together
+with torch's current HIP stream; the library never allocates or synchronises.
+If libmok.so is missing this module raises on import -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmok.so")
+
+F32, BF16, MXFP8 = 0, 1, 2
+FLAG_WGRAD_F32 = 1
+DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8}
+TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+STATUS = {0: "MOK_OK", 1: "MOK_ERR_NULL", 2: "MOK_ERR_ALIGN", 3: "MOK_ERR_SHAPE", 4: "MOK_ERR_DTYPE",
+          5: "MOK_ERR_HIP"}
+
+
+class MokError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status), text))
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("act", ctypes.c_int32), ("gemm", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("tile_m", ctypes.c_int32), ("grid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("sched", ctypes.c_size_t), ("saved", ctypes.c_size_t), ("fwd_ws", ctypes.c_size_t),
+                ("bwd_ws", ctypes.c_size_t)]
+
+
+class _SchedLayout(ctypes.Structure):
+    _fields_ = [("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t), ("tile_start", ctypes.c_size_t),
+                ("num_tiles", ctypes.c_size_t), ("perm", ctypes.c_size_t), ("inv", ctypes.c_size_t),
+                ("tiles", ctypes.c_size_t), ("tile_m", ctypes.c_int32), ("max_tiles", ctypes.c_int32)]
+
+
+class _SavedLayout(ctypes.Structure):
+    _fields_ = [("au_offset", ctypes.c_size_t), ("h_offset", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmok.so is not built (%s); run `python -m mixture_experts_layer_stable_amd.build`"
+                           % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(_Desc)
+    sig = {
+        "mok_workspace_query": [D, ctypes.POINTER(_Sizes)],
+        "mok_schedule_layout_query": [D, ctypes.POINTER(_SchedLayout)],
+        "mok_saved_layout_query": [D, ctypes.POINTER(_SavedLayout)],
+        "mok_route": [D, P, P, P, P, P, P, P],
+        "mok_schedule_build": [D, P, P, P],
+        "mok_moe_forward": [D, P, P, P, ctypes.POINTER(_Weights), P, P, P, P],
+        "mok_moe_backward": [D, P, P, P, P, ctypes.POINTER(_Weights), P, P, P, P, P, P, P, P, P, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.mok_status_string.argtypes = [ctypes.c_int]
+    lib.mok_status_string.restype = ctypes.c_char_p
+    lib.mok_version.argtypes = []
+    lib.mok_version.restype = ctypes.c_int32
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_route",
+           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_status_string", "mok_version")
+
+
+@dataclass
+class Desc:
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    act: int = BF16
+    gemm: Optional[int] = None
+    flags: int = 0
+    tile_m: int = 0
+    grid: int = 0
+
+    def c(self) -> _Desc:
+        g = self.act if self.gemm is None else self.gemm
+        return _Desc(self.T, self.H, self.E, self.k, self.I, self.act, g, self.flags, self.tile_m, self.grid, 0)
+
+    @property
+    def R(self) -> int:
+        return self.T * self.k
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return TORCH_DTYPE[self.act]
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise MokError(st, where, _lib.mok_status_string(st).decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version() -> int:
+    return _lib.mok_version()
+
+
+def workspace_query(d: Desc) -> dict:
+    s = _Sizes()
+    _check(_lib.mok_workspace_query(ctypes.byref(d.c()), ctypes.byref(s)), "mok_workspace_query")
+    return dict(sched=s.sched, saved=s.saved, fwd_ws=s.fwd_ws, bwd_ws=s.bwd_ws)
+
+
+def schedule_layout_query(d: Desc) -> dict:
+    s = _SchedLayout()
+    _check(_lib.mok_schedule_layout_query(ctypes.byref(d.c()), ctypes.byref(s)), "mok_schedule_layout_query")
+    return {n: getattr(s, n) for n, _ in _SchedLayout._fields_}
+
+
+def saved_layout_query(d: Desc) -> dict:
+    s = _SavedLayout()
+    _check(_lib.mok_saved_layout_query(ctypes.byref(d.c()), ctypes.byref(s)), "mok_saved_layout_query")
+    return dict(au_offset=s.au_offset, h_offset=s.h_offset)
+
+
+def route(d: Desc, x, wr, bias, idx, gate, logits=None, stream=None):
+    _check(_lib.mok_route(ctypes.byref(d.c()), _p(x), _p(wr), _p(bias), _p(idx), _p(gate), _p(logits),
+                          _stream(stream)), "mok_route")
+
+
+def schedule_build(d: Desc, idx, sched, stream=None):
+    _check(_lib.mok_schedule_build(ctypes.byref(d.c()), _p(idx), _p(sched), _stream(stream)), "mok_schedule_build")
+
+
+def moe_forward(d: Desc, sched, x, gate, w1, w2, y, saved, ws, stream=None):
+    w = _Weights(w1.data_ptr(), w2.data_ptr())
+    _check(_lib.mok_moe_forward(ctypes.byref(d.c()), _p(sched), _p(x), _p(gate), ctypes.byref(w), _p(y), _p(saved),
+                                _p(ws), _stream(stream)), "mok_moe_forward")
+
+
+def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws, stream=None):
+    w = _Weights(w1.data_ptr(), w2.data_ptr())
+    _check(_lib.mok_moe_backward(ctypes.byref(d.c()), _p(sched), _p(x), _p(idx), _p(gate), ctypes.byref(w), _p(wr),
+                                 _p(saved), _p(dy), _p(dx), _p(dw1), _p(dw2), _p(dgate), _p(dwr), _p(ws),
+                                 _stream(stream)), "mok_moe_backward")
+
+
+# ---------------------------------------------------------------------------
+# Convenience: the buffers one layer step needs, and views into them.
+# ---------------------------------------------------------------------------
+
+class Buffers:
+    """Caller-owned device buffers of one layer step (sizes from mok_workspace_query)."""
+
+    def __init__(self, d: Desc, device="cuda", backward=True, wgrad_f32=False):
+        sz = workspace_query(d)
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.desc = d
+        self.sched = torch.empty(max(sz["sched"], 256), **u8)
+        self.saved = torch.empty(max(sz["saved"], 256), **u8)
+        self.fwd_ws = torch.empty(max(sz["fwd_ws"], 256), **u8)
+        self.bwd_ws = torch.empty(max(sz["bwd_ws"], 256), **u8) if backward else None
+        f32 = dict(dtype=torch.float32, device=device)
+        self.idx = torch.empty(max(d.R, 4), dtype=torch.int32, device=device)[: d.R].view(d.T, d.k)
+        self.gate = torch.empty(max(d.R, 4), **f32)[: d.R].view(d.T, d.k)
+        self.y = torch.empty(d.T, d.H, dtype=d.dtype, device=device)
+        if backward:
+            wdt = torch.float32 if (wgrad_f32 or d.act == F32) else d.dtype
+            self.dx = torch.empty(d.T, d.H, dtype=d.dtype, device=device)
+            self.dgate = torch.empty(max(d.R, 4), **f32)[: d.R].view(d.T, d.k)
+            self.dw1 = torch.empty(d.E, 2 * d.I, d.H, dtype=wdt, device=device)
+            self.dw2 = torch.empty(d.E, d.H, d.I, dtype=wdt, device=device)
+            self.dwr = torch.empty(d.E, d.H, dtype=wdt, device=device)
+
+    def schedule_views(self) -> dict:
+        """int32 views of the schedule table's parts (for inspection and tests)."""
+        L = schedule_layout_query(self.desc)
+        d = self.desc
+        s = self.sched
+
+        def iv(off, n):
+            return s[off: off + 4 * n].view(torch.int32)
+
+        return dict(counts=iv(L["counts"], d.E), offsets=iv(L["offsets"], d.E + 1),
+                    tile_start=iv(L["tile_start"], d.E + 1), num_tiles=iv(L["num_tiles"], 1),
+                    perm=iv(L["perm"], d.R), inv=iv(L["inv"], d.R),
+                    tiles=iv(L["tiles"], 4 * L["max_tiles"]).view(-1, 4), tile_m=L["tile_m"],
+                    max_tiles=L["max_tiles"])
+
+    def saved_views(self) -> dict:
+        """a, u [R, I] and h [R, I] in routed-row order (views into `saved`)."""
+        L = saved_layout_query(self.desc)
+        d = self.desc
+        es = 4 if d.act == F32 else 2
+        au = self.saved[L["au_offset"]: L["au_offset"] + es * d.R * 2 * d.I].view(d.dtype).view(d.R, 2 * d.I)
+        h = self.saved[L["h_offset"]: L["h_offset"] + es * d.R * d.I].view(d.dtype).view(d.R, d.I)
+        return dict(a=au[:, : d.I], u=au[:, d.I:], h=h)
+
+
+def step(d: Desc, buf: Buffers, x, wr, bias, w1, w2, dy=None, stream=None, router_grad=True):
+    """route -> schedule -> forward (-> backward): one layer step, all on the GPU."""
+    route(d, x, wr, bias, buf.idx, buf.gate, None, stream)
+    schedule_build(d, buf.idx, buf.sched, stream)
+    moe_forward(d, buf.sched, x, buf.gate, w1, w2, buf.y, buf.saved, buf.fwd_ws, stream)
+    if dy is not None:
+        moe_backward(d, buf.sched, x, buf.idx, buf.gate, w1, w2, wr if router_grad else None, buf.saved, dy,
+                     buf.dx, buf.dw1, buf.dw2, buf.dgate, buf.dwr if router_grad else None, buf.bwd_ws, stream)

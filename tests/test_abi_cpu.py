@@ -1,0 +1,91 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/mok.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mok.h")
+
+
+@pytest.fixture(scope="module")
+def mok():
+    from mixture_experts_layer_stable_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from mixture_experts_layer_stable_amd import mok as m
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mok_status|const char\*|int32_t)\s+(mok_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("mok_route", "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_workspace_query"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mok):
+    lib = ctypes.CDLL(mok.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(mok.EXPORTS)
+    assert mok.version() == 100
+
+
+def test_status_strings(mok):
+    for st in range(6):
+        assert mok._lib.mok_status_string(st)
+
+
+def _d(mok, **kw):
+    base = dict(T=64, H=128, E=8, k=2, I=256, act=mok.BF16)
+    base.update(kw)
+    return mok.Desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), 3), (dict(k=9), 3), (dict(E=0), 3), (dict(E=1025), 3), (dict(k=17, E=32), 3),
+    (dict(H=100), 3), (dict(I=96), 3), (dict(T=-1), 3), (dict(tile_m=48), 3), (dict(grid=-2), 3),
+    (dict(act=2), 4), (dict(act=1, gemm=2), 4), (dict(T=1 << 29, k=8), 3),
+])
+def test_descriptor_validation(mok, kw, status):
+    with pytest.raises(mok.MokError) as ei:
+        mok.workspace_query(_d(mok, **kw))
+    assert ei.value.status == status
+
+
+def test_workspace_sizes_cover_worst_case(mok):
+    d = _d(mok, T=2048, H=1024, E=32, k=2, I=512)
+    s = mok.workspace_query(d)
+    R = d.R
+    assert s["sched"] >= 4 * (2 * R + 2 * d.E) + 16 * (R // 32 + d.E)
+    assert s["saved"] >= 2 * R * 3 * d.I
+    assert s["fwd_ws"] >= 2 * R * d.H
+    assert s["bwd_ws"] >= 2 * R * (2 * d.I + d.H) + 4 * R
+    lay = mok.saved_layout_query(d)
+    assert lay["h_offset"] >= 2 * R * 2 * d.I and lay["h_offset"] % 256 == 0
+
+
+def test_null_and_alignment_rejected_before_launch(mok):
+    d = _d(mok)
+    lib = mok._lib
+    c = d.c()
+    # x = NULL
+    st = lib.mok_route(ctypes.byref(c), None, ctypes.c_void_p(4096), None, ctypes.c_void_p(4096),
+                       ctypes.c_void_p(4096), None, None)
+    assert st == 1
+    # misaligned idx
+    st = lib.mok_route(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, ctypes.c_void_p(4100),
+                       ctypes.c_void_p(4096), None, None)
+    assert st == 2
+    # NULL schedule / weights struct
+    st = lib.mok_schedule_build(ctypes.byref(c), ctypes.c_void_p(4096), None, None)
+    assert st == 1
+    st = lib.mok_moe_forward(ctypes.byref(c), ctypes.c_void_p(4096), None, None, None, None, None, None, None)
+    assert st == 1

@@ -1,0 +1,182 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Integer results (routing indices, logits, counts, offsets, permutation, tiles)
+must match bit for bit; floating results within the relative Frobenius error
+of the storage format (bf16 5e-3, fp32 1e-5) against the oracle, which
+accumulates in fp64 and rounds at the same storage points.
+"""
+import numpy as np
+import pytest
+import torch
+
+from harness import TOL, Case, np64, rel_fro, run_gpu, run_oracle
+from mixture_experts_layer_stable_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_fp32", "small_bf16", "imbalanced_bf16"]
+
+
+def _w(name, **kw):
+    w = inputs.WORKLOADS[name]
+    return inputs.replace(w, **kw) if kw else w
+
+
+def _check_routing(g, o):
+    np.testing.assert_array_equal(g["logits"], o["z"])
+    np.testing.assert_array_equal(g["idx"], o["idx"])
+    assert rel_fro(g["gate"], o["gate"]) <= 1e-6
+    sc = o["sched"]
+    np.testing.assert_array_equal(g["counts"], sc["counts"])
+    np.testing.assert_array_equal(g["offsets"], sc["offsets"])
+    np.testing.assert_array_equal(g["perm"], sc["perm"])
+    np.testing.assert_array_equal(g["inv"], sc["inv"])
+    assert g["num_tiles"] == len(sc["tiles"])
+    np.testing.assert_array_equal(g["tiles"][: g["num_tiles"], :3], sc["tiles"])
+    np.testing.assert_array_equal(g["tile_start"][-1], len(sc["tiles"]))
+
+
+def _check_forward(w, g, o, tol):
+    fwd = o["fwd"]
+    perm = o["sched"]["perm"]
+    errs = {"y": rel_fro(np64(g["y"]), fwd["y"]),
+            "a": rel_fro(np64(g["a"]), fwd["a"][perm]),
+            "u": rel_fro(np64(g["u"]), fwd["u"][perm]),
+            "h": rel_fro(np64(g["h"]), fwd["h"][perm])}
+    for n, e in errs.items():
+        assert e <= tol, (n, e, errs)
+    return errs
+
+
+def _check_backward(w, g, o, tol, router=True):
+    b = o["bwd"]
+    dw1 = np.stack([b["dw1"][e] for e in range(w.E)])
+    dw2 = np.stack([b["dw2"][e] for e in range(w.E)])
+    errs = {"dx": rel_fro(np64(g["dx"]), b["dx"]),
+            "dw1": rel_fro(np64(g["dw1"]), dw1),
+            "dw2": rel_fro(np64(g["dw2"]), dw2),
+            "dgate": rel_fro(g["dgate"], b["dgate"])}
+    if router:
+        errs["dwr"] = rel_fro(np64(g["dwr"]), b["dwr"])
+    for n, e in errs.items():
+        assert e <= tol, (n, e, errs)
+    return errs
+
+
+def _full(w, case=None, tol=None, **kw):
+    case = case or Case(w)
+    g = run_gpu(case, backward=w.backward or kw.pop("backward", False), **kw)
+    o = run_oracle(case, backward="dx" in g, BM=g["tile_m"])
+    _check_routing(g, o)
+    tol = TOL[w.act] if tol is None else tol
+    _check_forward(w, g, o, tol)
+    if "dx" in g:
+        _check_backward(w, g, o, tol)
+    return g, o
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_parity(name):
+    """Every small workload end to end: routing bit-exact, forward (and backward) within tolerance."""
+    w = inputs.WORKLOADS[name]
+    print("case", name, flush=True)
+    _full(w)
+
+
+def test_tiny_fp32_backward_parity():
+    """The fp32 path also runs the backward (the tiny workload's step is forward-only)."""
+    w = _w("tiny_fp32", backward=True)
+    _full(w)
+
+
+@pytest.mark.parametrize("T,E,k,H,I", [(77, 5, 2, 128, 128), (130, 100, 3, 256, 384), (40, 600, 4, 128, 128),
+                                       (33, 8, 8, 128, 256), (50, 1, 1, 128, 128)])
+def test_ragged_and_odd_shapes(T, E, k, H, I):
+    """Token counts that are not tile multiples, E not a multiple of 64, E > 512, k = E, E = 1."""
+    w = _w("small_bf16", T=T, E=E, k=k, H=H, I=I)
+    print("case", w, flush=True)
+    _full(w)
+
+
+def test_all_tokens_one_expert():
+    """Worst-case imbalance: a +100 bias makes expert 3 every token's first choice (many tiles of
+    one expert); experts never chosen must get zero weight gradients."""
+    w = _w("small_bf16", T=300, E=16, k=2, H=128, I=128)
+    bias = torch.zeros(16, dtype=torch.float32)
+    bias[3] = 100.0
+    bias[10:] = -100.0
+    g, o = _full(w, Case(w, bias=bias))
+    assert g["counts"][3] == 300
+    assert np.all(g["counts"][10:] == 0)
+    assert np.all(np64(g["dw1"][10:]) == 0) and np.all(np64(g["dw2"][10:]) == 0)
+    assert np.all(np64(g["dwr"][10:]) == 0)
+
+
+def test_zero_tokens_and_duplicate_router_rows():
+    """x_t = 0 rows route to experts 0..k-1 with gates exactly 1/k; duplicated router rows tie and
+    the lower expert index wins."""
+    w = _w("small_bf16", T=64, E=8, k=2, H=128, I=128)
+    case = Case(w)
+    case.x[:10] = 0
+    case.wr[5] = case.wr[2]
+    g, o = _full(w, case)
+    np.testing.assert_array_equal(g["idx"][:10], np.tile([0, 1], (10, 1)))
+    assert np.all(g["gate"][:10] == 0.5)
+
+
+def test_empty_batch():
+    """T = 0: nothing to route; weight gradients are written as zeros."""
+    from mixture_experts_layer_stable_amd import mok
+    d = mok.Desc(0, 128, 4, 2, 128, act=mok.BF16)
+    buf = mok.Buffers(d, "cuda")
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    wr = torch.randn(4, 128, device="cuda").to(torch.bfloat16)
+    w1 = torch.randn(4, 256, 128, device="cuda").to(torch.bfloat16)
+    w2 = torch.randn(4, 128, 128, device="cuda").to(torch.bfloat16)
+    buf.dw1.fill_(1.0)
+    buf.dw2.fill_(1.0)
+    buf.dwr.fill_(1.0)
+    mok.step(d, buf, x, wr, None, w1, w2, dy=torch.empty(0, 128, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(buf.dw1 == 0) and torch.all(buf.dw2 == 0) and torch.all(buf.dwr == 0)
+    sv = buf.schedule_views()
+    assert int(sv["num_tiles"][0]) == 0 and torch.all(sv["counts"] == 0)
+
+
+def test_no_router_backward():
+    """wr = dwr = NULL skips the router backward: dx is the expert term only."""
+    w = _w("small_bf16", T=96, E=8, k=2, H=128, I=256)
+    case = Case(w)
+    g = run_gpu(case, router_grad=False)
+    o = run_oracle(case, BM=g["tile_m"], router_grad=False)
+    _check_routing(g, o)
+    _check_backward(w, g, o, TOL["bf16"], router=False)
+
+
+def test_wgrad_f32_flag():
+    """MOK_FLAG_WGRAD_F32 writes dW1/dW2/dWr in fp32 (compared to the fp64 oracle rounded to fp32)."""
+    w = _w("small_bf16", T=128, E=8, k=2, H=128, I=128)
+    case = Case(w)
+    g = run_gpu(case, wgrad_f32=True)
+    assert g["dw1"].dtype == torch.float32
+    o = run_oracle(case, BM=g["tile_m"], wfmt="f32")
+    b = o["bwd"]
+    assert rel_fro(np64(g["dw1"]), np.stack([b["dw1"][e] for e in range(8)])) <= 5e-3
+    assert rel_fro(np64(g["dwr"]), b["dwr"]) <= 5e-3
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "imbalanced_bf16"])
+def test_bit_reproducible_across_runs_tiles_and_grids(name):
+    """Two runs give identical bits; so do other schedule tile heights and persistent grid sizes
+    (every output element is summed in an order that does not depend on either)."""
+    w = inputs.WORKLOADS[name]
+    case = Case(w)
+    ref = run_gpu(case)
+    variants = [dict(), dict(tile_m=128), dict(tile_m=64, grid=7), dict(grid=300), dict(tile_m=32, grid=1)]
+    for kw in variants:
+        g = run_gpu(case, **kw)
+        for key in ("idx", "logits", "gate", "counts", "offsets", "perm", "inv", "dgate"):
+            np.testing.assert_array_equal(g[key], ref[key], err_msg=str((kw, key)))
+        for key in ("y", "a", "u", "h", "dx", "dw1", "dw2", "dwr"):
+            assert torch.equal(g[key].view(torch.int16) if g[key].dtype == torch.bfloat16 else g[key],
+                               ref[key].view(torch.int16) if ref[key].dtype == torch.bfloat16 else ref[key]), (kw, key)
