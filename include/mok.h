@@ -24,9 +24,10 @@
  *  - T tokens, hidden size H, E experts, top-k routing (k slots per token),
  *    expert intermediate size I.  R = T*k routed rows.  Flat slot s = t*k + j.
  *  - All arrays are row-major, device memory, 16-byte aligned, owned by the
- *    caller.  The library never allocates, frees or synchronises; every call
- *    only enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
- *    and returns.  Nothing is read back to the host.
+ *    caller.  A pointer to an array of zero elements (T = 0) may be NULL.
+ *    The library never allocates, frees or synchronises; every call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = default stream) and
+ *    returns.  Nothing is read back to the host.
  *  - Activation dtype `act` (MOK_F32 or MOK_BF16) is the storage type of
  *    x, y, dy, dx, the router weight wr, the expert weights and every saved or
  *    intermediate activation.  All arithmetic accumulates in fp32.
@@ -187,6 +188,22 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
                             const float* gate, const mok_weights* w, const void* wr, const void* saved,
                             const void* dy, void* dx, void* dw1, void* dw2, float* dgate, void* dwr, void* ws,
                             void* stream);
+
+/*
+ * Measurement aid (process-wide state, not thread-safe). While set, every
+ * launch of the kernel group `name` -- one of "route", "schedule", "fc1",
+ * "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "dw2", "dw1",
+ * "dwr", or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
+ * and hipEventRecord(events[2n+1]) after it on the launch stream, for
+ * n = 0, 1, ... < capacity; later launches are not bracketed.  `events` are
+ * caller-created hipEvent_t handles.  name == NULL ends tracing.  The trace
+ * never synchronises; elapsed times are read by the caller.
+ */
+mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity);
+/* Launches bracketed since the last mok_trace_set. */
+int32_t mok_trace_count(void);
+/* Kernel group of the n-th bracketed launch (static string), or NULL. */
+const char* mok_trace_name(int32_t n);
 
 /* Static string naming a status code. */
 const char* mok_status_string(mok_status s);

@@ -1,5 +1,6 @@
 // C-ABI entry points of libmok: argument checks, buffer layouts, launches.
 #include <mutex>
+#include <string>
 
 #include "kernels.h"
 
@@ -144,9 +145,34 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
     if (!aligned16(p)) return MOK_ERR_ALIGN; \
   } while (0)
 
-#define MOK_HIP(call)                              \
-  do {                                             \
-    if ((call) != hipSuccess) return MOK_ERR_HIP;  \
+// ---- measurement trace (see mok_trace_set) ----
+struct Trace {
+  std::string filter;
+  void* const* events = nullptr;
+  int cap = 0;
+  int count = 0;
+  const char* names[4096];
+};
+Trace g_trace;
+
+bool trace_on(const char* name) {
+  return g_trace.events != nullptr && g_trace.count < g_trace.cap &&
+         (g_trace.filter == "*" || g_trace.filter == name);
+}
+
+// Launch `call` (a hipError_t expression) bracketed by trace events when traced.
+#define MOK_LAUNCH(name, stream, call)                                                              \
+  do {                                                                                              \
+    const bool tr_ = trace_on(name);                                                                \
+    if (tr_ && hipEventRecord((hipEvent_t)g_trace.events[2 * g_trace.count], stream) != hipSuccess) \
+      return MOK_ERR_HIP;                                                                           \
+    if ((call) != hipSuccess) return MOK_ERR_HIP;                                                   \
+    if (tr_) {                                                                                      \
+      if (hipEventRecord((hipEvent_t)g_trace.events[2 * g_trace.count + 1], stream) != hipSuccess)  \
+        return MOK_ERR_HIP;                                                                         \
+      if (g_trace.count < 4096) g_trace.names[g_trace.count] = name;                                \
+      ++g_trace.count;                                                                              \
+    }                                                                                               \
   } while (0)
 
 }  // namespace
@@ -197,6 +223,7 @@ mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const flo
                      float* logits, void* stream) {
   mok_status st = check_desc(d);
   if (st != MOK_OK) return st;
+  if (d->T == 0) return MOK_OK;  // empty arrays may be NULL
   MOK_REQUIRE(x);
   MOK_REQUIRE(wr);
   MOK_REQUIRE(idx);
@@ -211,7 +238,7 @@ mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const flo
   c.I = d->I;
   c.act = d->act;
   c.s = (hipStream_t)stream;
-  MOK_HIP(launch_route(c, x, wr, bias, idx, gate, logits));
+  MOK_LAUNCH("route", c.s, launch_route(c, x, wr, bias, idx, gate, logits));
   return MOK_OK;
 }
 
@@ -221,7 +248,7 @@ mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched
   mok_status st = make_ctx(d, sched, stream, &c);
   if (st != MOK_OK) return st;
   if (c.R > 0) MOK_REQUIRE(idx);
-  MOK_HIP(launch_schedule(c, idx));
+  MOK_LAUNCH("schedule", c.s, launch_schedule(c, idx));
   return MOK_OK;
 }
 
@@ -242,9 +269,9 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
   MOK_REQUIRE(ws);
   const Layout L = layout_of(d, c.BM);
   char* sv = (char*)saved;
-  MOK_HIP(launch_fc1(c, x, w->w1, sv + L.au, sv + L.h));
-  MOK_HIP(launch_fc2(c, sv + L.h, w->w2, ws));
-  MOK_HIP(launch_combine(c, ws, gate, y));
+  MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, sv + L.au, sv + L.h));
+  MOK_LAUNCH("fc2", c.s, launch_fc2(c, sv + L.h, w->w2, ws));
+  MOK_LAUNCH("combine", c.s, launch_combine(c, ws, gate, y));
   return MOK_OK;
 }
 
@@ -279,16 +306,35 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
   float* dgp = (float*)(wb + L.dgp);
   float* dz = (float*)(wb + L.dz);
   if (c.R > 0) {
-    MOK_HIP(launch_dh(c, dy, w->w2, sv + L.au, sv + L.h, gate, wb + L.dgu, dgp));
-    MOK_HIP(launch_router_bwd(c, dgp, gate, dgate, dz));
-    MOK_HIP(launch_dx(c, wb + L.dgu, w->w1, wb + L.bpart));
-    MOK_HIP(launch_dx_reduce(c, wb + L.bpart, dz, idx, wr, dx));
+    MOK_LAUNCH("dh", c.s, launch_dh(c, dy, w->w2, sv + L.au, sv + L.h, gate, wb + L.dgu, dgp));
+    MOK_LAUNCH("router_bwd", c.s, launch_router_bwd(c, dgp, gate, dgate, dz));
+    MOK_LAUNCH("dx", c.s, launch_dx(c, wb + L.dgu, w->w1, wb + L.bpart));
+    MOK_LAUNCH("dx_reduce", c.s, launch_dx_reduce(c, wb + L.bpart, dz, idx, wr, dx));
   }
-  MOK_HIP(launch_dw2(c, dy, gate, sv + L.h, dw2));
-  MOK_HIP(launch_dw1(c, wb + L.dgu, x, dw1));
-  if (dwr != nullptr) MOK_HIP(launch_dwr(c, dz, x, dwr));
+  MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, sv + L.h, dw2));
+  MOK_LAUNCH("dw1", c.s, launch_dw1(c, wb + L.dgu, x, dw1));
+  if (dwr != nullptr) MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr));
   return MOK_OK;
 }
+
+mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity) {
+  if (name == nullptr) {
+    g_trace.events = nullptr;
+    g_trace.cap = 0;
+    return MOK_OK;
+  }
+  if (events == nullptr) return MOK_ERR_NULL;
+  if (capacity < 0) return MOK_ERR_SHAPE;
+  g_trace.filter = name;
+  g_trace.events = events;
+  g_trace.cap = std::min(capacity, 4096);
+  g_trace.count = 0;
+  return MOK_OK;
+}
+
+int32_t mok_trace_count(void) { return g_trace.count; }
+
+const char* mok_trace_name(int32_t n) { return (n >= 0 && n < g_trace.count && n < 4096) ? g_trace.names[n] : nullptr; }
 
 const char* mok_status_string(mok_status s) {
   switch (s) {

@@ -81,12 +81,19 @@ def _load():
     lib.mok_status_string.restype = ctypes.c_char_p
     lib.mok_version.argtypes = []
     lib.mok_version.restype = ctypes.c_int32
+    lib.mok_trace_set.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    lib.mok_trace_set.restype = ctypes.c_int
+    lib.mok_trace_count.argtypes = []
+    lib.mok_trace_count.restype = ctypes.c_int32
+    lib.mok_trace_name.argtypes = [ctypes.c_int32]
+    lib.mok_trace_name.restype = ctypes.c_char_p
     return lib
 
 
 _lib = _load()
 EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_route",
-           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_status_string", "mok_version")
+           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_status_string", "mok_version",
+           "mok_trace_set", "mok_trace_count", "mok_trace_name")
 
 
 @dataclass
@@ -171,6 +178,40 @@ def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, d
     _check(_lib.mok_moe_backward(ctypes.byref(d.c()), _p(sched), _p(x), _p(idx), _p(gate), ctypes.byref(w), _p(wr),
                                  _p(saved), _p(dy), _p(dx), _p(dw1), _p(dw2), _p(dgate), _p(dwr), _p(ws),
                                  _stream(stream)), "mok_moe_backward")
+
+
+class KernelTrace:
+    """Bracket launches of one kernel group (or "*") with HIP events (mok_trace_set).
+
+    with KernelTrace("fc1", capacity=64) as tr:
+        ... launches ...
+    tr.durations_ms()  -> [(name, ms), ...]   (synchronises on the events)
+    """
+
+    def __init__(self, name: str, capacity: int = 256):
+        self.name = name
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * capacity)]
+        for e in self.events:        # materialise the underlying hipEvent_t
+            e.record()
+        torch.cuda.synchronize()
+        self._handles = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        self.capacity = capacity
+        self.count = 0
+        self.names = []
+
+    def __enter__(self):
+        _check(_lib.mok_trace_set(self.name.encode(), self._handles, self.capacity), "mok_trace_set")
+        return self
+
+    def __exit__(self, *exc):
+        self.count = _lib.mok_trace_count()
+        self.names = [_lib.mok_trace_name(i).decode() for i in range(self.count)]
+        _lib.mok_trace_set(None, None, 0)
+        return False
+
+    def durations_ms(self):
+        self.events[2 * max(self.count, 1) - 1].synchronize()
+        return [(self.names[i], self.events[2 * i].elapsed_time(self.events[2 * i + 1])) for i in range(self.count)]
 
 
 # ---------------------------------------------------------------------------
