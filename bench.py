@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--config", default="kimi_k2_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (known bytes, for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the layer step; multi-GPU runs (--gpus %d) are not part of "
@@ -157,6 +159,12 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 512, "imbalanced_bf16": 512}.get(w.name, 6)
     keep = cpu_sample_plan(w, ntok) if not args.no_cpu_baseline else []
