@@ -100,7 +100,8 @@ typedef struct mok_sizes {
   size_t sched;  /* schedule table (mok_schedule_build)                        */
   size_t saved;  /* forward activations kept for the backward pass              */
   size_t fwd_ws; /* forward scratch: per-(token,slot) partial rows [R][H]       */
-  size_t bwd_ws; /* backward scratch: dGU [R][2I], partials [R][H], d-gate parts */
+  size_t bwd_ws; /* backward scratch: dGU [R][2I], partials [R][H], d-gate parts,
+                    and for bf16 the routed-order rows of x and g*dy [R][H] each */
 } mok_sizes;
 
 /* Byte offsets of the schedule table's parts inside the schedule buffer.
@@ -192,8 +193,8 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
 /*
  * Measurement aid (process-wide state, not thread-safe). While set, every
  * launch of the kernel group `name` -- one of "route", "schedule", "fc1",
- * "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "dw2", "dw1",
- * "dwr", or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
+ * "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "gather", "dw2",
+ * "dw1", "dwr", or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
  * and hipEventRecord(events[2n+1]) after it on the launch stream, for
  * n = 0, 1, ... < capacity; later launches are not bracketed.  `events` are
  * caller-created hipEvent_t handles.  name == NULL ends tracing.  The trace

@@ -64,7 +64,7 @@ struct Layout {
   size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, sched;
   size_t au, h, saved;
   size_t fwd_part, fwd;
-  size_t dgu, bpart, dgp, dz, bwd;
+  size_t dgu, bpart, dgp, dz, xs, dos, bwd;
 };
 
 // Buffer layouts. The schedule is sized for the smallest tile height, so its
@@ -96,6 +96,10 @@ Layout layout_of(const mok_desc* d, int BM) {
   L.bpart = o; o = up(o + es * (size_t)R * d->H);
   L.dgp = o; o = up(o + 4 * (size_t)R * dh_ntiles(d->I));
   L.dz = o; o = up(o + 4 * (size_t)R);
+  // bf16: token rows in routed order for the weight-gradient GEMMs (x and g*dy)
+  const size_t rows = d->act == MOK_BF16 ? es * (size_t)R * d->H : 0;
+  L.xs = o; o = up(o + rows);
+  L.dos = o; o = up(o + rows);
   L.bwd = o;
   return L;
 }
@@ -311,8 +315,15 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
     MOK_LAUNCH("dx", c.s, launch_dx(c, wb + L.dgu, w->w1, wb + L.bpart));
     MOK_LAUNCH("dx_reduce", c.s, launch_dx_reduce(c, wb + L.bpart, dz, idx, wr, dx));
   }
-  MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, sv + L.h, dw2));
-  MOK_LAUNCH("dw1", c.s, launch_dw1(c, wb + L.dgu, x, dw1));
+  if (c.act == MOK_BF16) {
+    MOK_LAUNCH("gather", c.s, launch_gather_rows(c, dy, gate, wb + L.dos));
+    MOK_LAUNCH("gather", c.s, launch_gather_rows(c, x, nullptr, wb + L.xs));
+    MOK_LAUNCH("dw2", c.s, launch_dw2_bf16(c, wb + L.dos, sv + L.h, dw2));
+    MOK_LAUNCH("dw1", c.s, launch_dw1_bf16(c, wb + L.dgu, wb + L.xs, dw1));
+  } else {
+    MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, sv + L.h, dw2));
+    MOK_LAUNCH("dw1", c.s, launch_dw1(c, wb + L.dgu, x, dw1));
+  }
   if (dwr != nullptr) MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr));
   return MOK_OK;
 }

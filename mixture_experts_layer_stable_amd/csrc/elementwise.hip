@@ -115,7 +115,36 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dz, 
   for (int q = 0; q < VE; ++q) Elem<TO>::put(o, q, acc[q]);
 }
 
+// dst[r] = src[perm[r] / k] (* gate[perm[r]], rounded to bf16): token rows in routed order.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16* __restrict__ src, const int32_t* __restrict__ perm,
+                                                          const float* __restrict__ gate, bf16* __restrict__ dst, int R,
+                                                          int H, int k) {
+  const int vpr = H / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)R * vpr) return;
+  const int r = (int)(gid / vpr);
+  const int h0 = (int)(gid - (int64_t)r * vpr) * 8;
+  const int s = perm[r];
+  uint4 v = ldg16(src + (int64_t)(s / k) * H + h0);
+  if (gate != nullptr) {
+    const float g = gate[s];
+    float f[8];
+    unpack(v, f, (bf16*)nullptr);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f[q] = g * f[q];
+    v = pack(f, (bf16*)nullptr);
+  }
+  stg16(dst + (int64_t)r * H + h0, v);
+}
+
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+hipError_t launch_gather_rows(const Ctx& c, const void* src, const float* gate, void* dst) {
+  if (c.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks_for((int64_t)c.R * (c.H / 8))), dim3(256), 0, c.s,
+                     (const bf16*)src, c.perm, gate, (bf16*)dst, c.R, c.H, c.k);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const Ctx& c, const void* part, const float* gate, void* y) {
   if (c.T == 0) return hipSuccess;

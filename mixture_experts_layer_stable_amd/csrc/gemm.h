@@ -86,15 +86,18 @@ struct KLoader {
 // src(k, mn0) -> uint4 holding elements mn0 .. mn0+VE-1 at row k (zeros past
 // the end of K). Blocks of VE (k) x VE (mn) per thread, transposed in registers.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// v[q] holds 8 consecutive mn at k = q; o[j] receives 8 consecutive k at mn = j.
 __device__ __forceinline__ void transpose8x8_b16(const uint4 (&v)[8], uint4 (&o)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t* a = reinterpret_cast<const uint32_t*>(&v[2 * d]);
-      const uint32_t* b = reinterpret_cast<const uint32_t*>(&v[2 * d + 1]);
-      const uint32_t x = a[j >> 1], y = b[j >> 1];
+      const uint32_t x = word(v[2 * d], j >> 1), y = word(v[2 * d + 1], j >> 1);
       w[d] = (j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
     }
     o[j] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -102,13 +105,7 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&v)[8], uint4 (&o)
 }
 __device__ __forceinline__ void transpose4x4_b32(const uint4 (&v)[4], uint4 (&o)[4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&v[0]);
-    const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v[1]);
-    const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&v[2]);
-    const uint32_t* a3 = reinterpret_cast<const uint32_t*>(&v[3]);
-    o[j] = make_uint4(a0[j], a1[j], a2[j], a3[j]);
-  }
+  for (int j = 0; j < 4; ++j) o[j] = make_uint4(word(v[0], j), word(v[1], j), word(v[2], j), word(v[3], j));
 }
 
 template <typename T, int ROWS>
@@ -310,6 +307,90 @@ __device__ __forceinline__ void for_each_row_tile(const Sched& sc, const int* s_
 __device__ __forceinline__ void load_tile_start(const Sched& sc, int* s_ts) {
   for (int i = threadIdx.x; i <= sc.E; i += blockDim.x) s_ts[i] = sc.tile_start[i];
   __syncthreads();
+}
+
+}  // namespace mok
+
+namespace mok {
+
+// Epilogue staging: each wave copies one (or a pair of) 32x32 accumulator
+// block(s) through its own LDS patch and hands them back with every lane
+// owning 16 consecutive columns of one row, so global accesses are 16-byte
+// vectors. Call after main_loop (smem is free); all waves must call it.
+//   f(row, col, g, u): row/col are workgroup-tile coordinates of the first of
+//   the lane's 16 columns; g[16] = block fn values; u[16] = block fn+1 values
+//   when PAIR (the SwiGLU up half), otherwise unused.
+constexpr int kPatchLd = 68;  // floats per patch row: 64 columns + 4 pad
+
+template <class Tl, bool PAIR, class F>
+__device__ __forceinline__ void epilogue16(f32x16_t (&acc)[Tl::FM][Tl::FN], char* smem, int wave, int wm, int wn,
+                                           int lane, F&& f) {
+  float* patch = reinterpret_cast<float*>(smem) + wave * (32 * kPatchLd);
+  constexpr int STEP = PAIR ? 2 : 1;
+#pragma unroll
+  for (int fm = 0; fm < Tl::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; fn += STEP) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        patch[row * kPatchLd + (lane & 31)] = acc[fm][fn][r];
+        if constexpr (PAIR) patch[row * kPatchLd + 32 + (lane & 31)] = acc[fm][fn + 1][r];
+      }
+      __syncthreads();
+      const int row = lane >> 1, c0 = (lane & 1) * 16;
+      float g[16], u[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(patch + row * kPatchLd + c0 + 4 * q);
+        g[4 * q] = a.x; g[4 * q + 1] = a.y; g[4 * q + 2] = a.z; g[4 * q + 3] = a.w;
+        if constexpr (PAIR) {
+          const float4 b = *reinterpret_cast<const float4*>(patch + row * kPatchLd + 32 + c0 + 4 * q);
+          u[4 * q] = b.x; u[4 * q + 1] = b.y; u[4 * q + 2] = b.z; u[4 * q + 3] = b.w;
+        }
+      }
+      f(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c0, g, u);
+      __syncthreads();
+    }
+}
+
+// 16 values -> two 16-byte vectors of T at p (8 bf16 each) or four (fp32).
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const float (&v)[16]);
+template <>
+__device__ __forceinline__ void store16<bf16>(bf16* p, const float (&v)[16]) {
+  float a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { a[i] = v[i]; b[i] = v[8 + i]; }
+  stg16(p, pack(a, (bf16*)nullptr));
+  stg16(p + 8, pack(b, (bf16*)nullptr));
+}
+template <>
+__device__ __forceinline__ void store16<float>(float* p, const float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) stg16(p + 4 * q, make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                                                          __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])));
+}
+
+// 16 consecutive elements of T at p -> floats.
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&v)[16]);
+template <>
+__device__ __forceinline__ void load16<bf16>(const bf16* p, float (&v)[16]) {
+  float a[8], b[8];
+  unpack(ldg16(p), a, (bf16*)nullptr);
+  unpack(ldg16(p + 8), b, (bf16*)nullptr);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { v[i] = a[i]; v[8 + i] = b[i]; }
+}
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w = ldg16(p + 4 * q);
+    v[4 * q] = __uint_as_float(w.x); v[4 * q + 1] = __uint_as_float(w.y);
+    v[4 * q + 2] = __uint_as_float(w.z); v[4 * q + 3] = __uint_as_float(w.w);
+  }
 }
 
 }  // namespace mok

@@ -1,0 +1,282 @@
+// bf16 grouped expert GEMMs on the direct-to-LDS core (gemm2.h).
+//
+// Row GEMMs (M = routed rows of one schedule tile, persistent, XCD-partitioned,
+// expert-major tile walk):
+//   fc1  pull dispatch: A = x rows gathered through perm; B = W1[e] rows with
+//        gate/up interleaved per 32-column block; SwiGLU epilogue (h = silu(a)*u).
+//   fc2  A = h rows; B = W2[e] rows; o written to the (token, slot) partial row.
+//   dh   pull reverse-combine: A = dY rows gathered through perm; B = W2[e] read
+//        transposed (MN-contiguous); epilogue: SwiGLU backward + gate-gradient
+//        partials (router-weight gradients fused into the SwiGLU backward,
+//        dothoosh.com MoK page, "Technical details of the MoK mechanism").
+//   dx   push reverse-dispatch: A = dGU rows; B = W1[e] read transposed; q
+//        written to the (token, slot) partial row.
+// Weight gradients (one workgroup per output tile, XCD-grouped by expert):
+//   dw2  dW2[e] = sum over e's routed rows of dO_r^T h_r, dO = g*dY gathered.
+//   dw1  dW1[e] = sum over e's routed rows of dGU_r^T x_r, x gathered.
+//   Both operands are token-major rows (MN-contiguous, K = routed rows),
+//   K-tail rows read from a zero block.
+#include "gemm2.h"
+#include "kernels.h"
+
+namespace mok {
+
+__device__ uint4 g_zero_1k[64] = {};
+
+constexpr int kMaxE2 = 1024;
+constexpr int kRowStages = 3;
+constexpr int kDwStages = 3;
+
+template <int BM, int BN>
+using RowTiling2 = Tiling<BM, BN, (BM == 128 ? 2 : 1), (BM == 128 ? 2 : 4)>;
+
+struct RowArgs {
+  Sched sc;
+  const bf16* a;     // fc1: x; fc2: h; dh: dy; dx: dgu
+  const bf16* w;     // fc1: w1; fc2: w2; dh: w2; dx: w1
+  bf16* out0;        // fc1: au; fc2/dx: part; dh: dgu
+  bf16* out1;        // fc1: h
+  const bf16* au;    // dh
+  const bf16* h;     // dh
+  const float* gate; // dh
+  float* dgp;        // dh
+  int H, I, k, R;
+};
+
+enum RowKind { FC1 = 0, FC2 = 1, DH = 2, DX = 3 };
+
+template <int KIND, class Tl>
+__global__ __launch_bounds__(256) void row_gemm2_kernel(RowArgs a) {
+  using OA = OpK<Tl::BM>;
+  constexpr bool B_MN = KIND == DH || KIND == DX;
+  using OB = typename std::conditional<B_MN, OpMN<Tl::BN, 64>, OpK<Tl::BN>>::type;
+  constexpr int SB = OA::BYTES + OB::BYTES;
+  __shared__ __align__(1024) char smem[kRowStages * SB];
+  __shared__ int s_ts[kMaxE2 + 1];
+  __shared__ int s_slot[Tl::BM];
+  __shared__ float s_red[KIND == DH ? Tl::BN / 32 : 1][KIND == DH ? Tl::BM : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  const int I2 = 2 * a.I;
+  // N of the GEMM and its tile count; K
+  const int N = KIND == FC1 ? I2 : (KIND == FC2 || KIND == DX ? a.H : a.I);
+  const int K = KIND == FC1 || KIND == DH ? a.H : (KIND == FC2 ? a.I : I2);
+  load_tile_start(a.sc, s_ts);
+  for_each_row_tile(a.sc, s_ts, N / Tl::BN, [&](const RowTile& t) {
+    __syncthreads();
+    for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
+    __syncthreads();
+    OA oa;
+    oa.init(wave, lane, [&](int row) -> const bf16* {
+      const int r = row < t.nrows ? row : 0;  // padding rows re-read row 0 (finite; their outputs are dropped)
+      if constexpr (KIND == FC1 || KIND == DH) return a.a + (int64_t)(s_slot[r] / a.k) * a.H;
+      else return a.a + (int64_t)(t.row0 + r) * K;
+    });
+    OB ob;
+    if constexpr (B_MN) {
+      // dh: W2[e] [H][I], k = h, columns i; dx: W1[e] [2I][H], k = c, columns h
+      const bf16* base = KIND == DH ? a.w + (int64_t)t.e * a.H * a.I + t.n * Tl::BN
+                                    : a.w + (int64_t)t.e * I2 * a.H + t.n * Tl::BN;
+      ob.init(base, 2 * (int64_t)(KIND == DH ? a.I : a.H), K, wave, lane);
+    } else if constexpr (KIND == FC1) {
+      const int cbase = t.n * (Tl::BN / 2);
+      ob.init(wave, lane, [&](int j) -> const bf16* {
+        const int wj = j / Tl::WTN, fn = (j % Tl::WTN) >> 5;
+        const int c = cbase + wj * (Tl::WTN / 2) + (fn >> 1) * 32 + (j & 31);
+        return a.w + ((int64_t)t.e * I2 + ((fn & 1) ? a.I + c : c)) * a.H;
+      });
+    } else {
+      ob.init(wave, lane, [&](int j) -> const bf16* { return a.w + ((int64_t)t.e * a.H + t.n * Tl::BN + j) * a.I; });
+    }
+    f32x16_t acc[Tl::FM][Tl::FN];
+    main_loop2<Tl, kRowStages>(oa, ob, K / 64, smem, wave, wm, wn, lane, acc);
+
+    if constexpr (KIND == FC1) {
+      const int cbase = t.n * (Tl::BN / 2);
+      epilogue16<Tl, true>(acc, smem, wave, wm, wn, lane,
+                           [&](int row, int col, const float (&g)[16], const float (&u)[16]) {
+        if (row >= t.nrows) return;
+        const int64_t R = t.row0 + row;
+        const int wj = col / Tl::WTN, cw = col % Tl::WTN;
+        const int c = cbase + wj * (Tl::WTN / 2) + (cw >> 6) * 32 + (cw & 31);
+        float hv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+        store16<bf16>(a.out0 + R * I2 + c, g);
+        store16<bf16>(a.out0 + R * I2 + a.I + c, u);
+        store16<bf16>(a.out1 + R * a.I + c, hv);
+      });
+    } else if constexpr (KIND == FC2 || KIND == DX) {
+      epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane,
+                            [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+        if (row < t.nrows) store16<bf16>(a.out0 + (int64_t)s_slot[row] * a.H + t.n * Tl::BN + col, g);
+      });
+    } else {  // DH
+      epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane,
+                            [&](int row, int col, const float (&dA)[16], const float (&)[16]) {
+        float part = 0.0f;
+        if (row < t.nrows) {
+          const int64_t R = t.row0 + row;
+          const int c = t.n * Tl::BN + col;
+          const float g = a.gate[s_slot[row]];
+          float av[16], uv[16], hv[16], da[16], du[16];
+          load16<bf16>(a.au + R * I2 + c, av);
+          load16<bf16>(a.au + R * I2 + a.I + c, uv);
+          load16<bf16>(a.h + R * a.I + c, hv);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            part = __builtin_fmaf(dA[i], hv[i], part);
+            const float dh = g * dA[i];
+            const float sg = 1.0f / (1.0f + expf(-av[i]));
+            da[i] = dh * uv[i] * sg * (1.0f + av[i] * (1.0f - sg));
+            du[i] = dh * av[i] * sg;
+          }
+          store16<bf16>(a.out0 + R * I2 + c, da);
+          store16<bf16>(a.out0 + R * I2 + a.I + c, du);
+        }
+        const float other = __shfl_xor(part, 1);
+        const float blk = (lane & 1) ? other + part : part + other;
+        if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+      });
+      for (int i = tid; i < t.nrows; i += kThreads) {
+        float s = 0.0f;
+#pragma unroll
+        for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
+        a.dgp[(int64_t)t.n * a.R + t.row0 + i] = s;
+      }
+    }
+  });
+}
+
+struct DwArgs2 {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const bf16* arows;  // dw2: dO rows [R][H]; dw1: dGU rows [R][2I]
+  const bf16* brows;  // dw2: h rows [R][I];  dw1: x rows [R][H]
+  void* out;
+  int M, N;           // dw2: H, I; dw1: 2I, H
+  int lda, ldb;       // elements per routed row of arows / brows
+};
+
+template <class Tl, typename TO>
+__global__ __launch_bounds__(256) void dw_gemm2_kernel(DwArgs2 a) {
+  using OA = OpMN<Tl::BM, 32>;
+  using OB = OpMN<Tl::BN, 32>;
+  __shared__ __align__(1024) char smem[kDwStages * (OA::BYTES + OB::BYTES)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  const int e = L / (MT * NT);
+  const int rem = L - e * MT * NT;
+  const int mt = rem / NT, nt = rem - mt * NT;
+  const int seg0 = a.offsets[e], cnt = a.counts[e];
+  OA oa;
+  oa.init(a.arows + (int64_t)seg0 * a.lda + mt * Tl::BM, 2 * (int64_t)a.lda, cnt, wave, lane);
+  OB ob;
+  ob.init(a.brows + (int64_t)seg0 * a.ldb + nt * Tl::BN, 2 * (int64_t)a.ldb, cnt, wave, lane);
+  f32x16_t acc[Tl::FM][Tl::FN];
+  main_loop2<Tl, kDwStages>(oa, ob, (cnt + 31) / 32, smem, wave, wm, wn, lane, acc);
+  TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
+  epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+    store16<TO>(out + (int64_t)row * a.N + col, g);
+  });
+}
+
+// ---------------------------------------------------------------------------
+static Sched sched_of2(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+
+template <int KIND, int BM, int BN>
+static hipError_t row_launch(const Ctx& c, const RowArgs& a, int N) {
+  using Tl = RowTiling2<BM, BN>;
+  int g = c.grid > 0 ? c.grid : c.num_cu;
+  const int64_t upper = (int64_t)c.max_tiles * (N / BN);
+  if (g > upper) g = (int)std::max<int64_t>(upper, 1);
+  hipLaunchKernelGGL((row_gemm2_kernel<KIND, Tl>), dim3(g), dim3(kThreads), 0, c.s, a);
+  return hipGetLastError();
+}
+
+template <int KIND, int BN>
+static hipError_t row_bm(const Ctx& c, const RowArgs& a, int N) {
+  switch (c.BM) {
+    case 32: return row_launch<KIND, 32, BN>(c, a, N);
+    case 64: return row_launch<KIND, 64, BN>(c, a, N);
+    case 128: return row_launch<KIND, 128, BN>(c, a, N);
+  }
+  return hipErrorInvalidValue;
+}
+
+static RowArgs row_args(const Ctx& c) {
+  RowArgs a{};
+  a.sc = sched_of2(c);
+  a.H = c.H;
+  a.I = c.I;
+  a.k = c.k;
+  a.R = c.R;
+  return a;
+}
+
+hipError_t launch_fc1_bf16(const Ctx& c, const void* x, const void* w1, void* au, void* h) {
+  RowArgs a = row_args(c);
+  a.a = (const bf16*)x;
+  a.w = (const bf16*)w1;
+  a.out0 = (bf16*)au;
+  a.out1 = (bf16*)h;
+  return row_bm<FC1, 256>(c, a, 2 * c.I);
+}
+
+hipError_t launch_fc2_bf16(const Ctx& c, const void* h, const void* w2, void* part) {
+  RowArgs a = row_args(c);
+  a.a = (const bf16*)h;
+  a.w = (const bf16*)w2;
+  a.out0 = (bf16*)part;
+  return bn_rows(c.H) == 256 ? row_bm<FC2, 256>(c, a, c.H) : row_bm<FC2, 128>(c, a, c.H);
+}
+
+hipError_t launch_dh_bf16(const Ctx& c, const void* dy, const void* w2, const void* au, const void* h,
+                          const float* gate, void* dgu, float* dgp) {
+  RowArgs a = row_args(c);
+  a.a = (const bf16*)dy;
+  a.w = (const bf16*)w2;
+  a.out0 = (bf16*)dgu;
+  a.au = (const bf16*)au;
+  a.h = (const bf16*)h;
+  a.gate = gate;
+  a.dgp = dgp;
+  return bn_rows(c.I) == 256 ? row_bm<DH, 256>(c, a, c.I) : row_bm<DH, 128>(c, a, c.I);
+}
+
+hipError_t launch_dx_bf16(const Ctx& c, const void* dgu, const void* w1, void* part) {
+  RowArgs a = row_args(c);
+  a.a = (const bf16*)dgu;
+  a.w = (const bf16*)w1;
+  a.out0 = (bf16*)part;
+  return bn_rows(c.H) == 256 ? row_bm<DX, 256>(c, a, c.H) : row_bm<DX, 128>(c, a, c.H);
+}
+
+template <class Tl>
+static hipError_t dw_launch(const Ctx& c, const DwArgs2& a) {
+  const int64_t blocks = (int64_t)c.E * (a.M / Tl::BM) * (a.N / Tl::BN);
+  if (c.wgrad_f32)
+    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, float>), dim3((unsigned)blocks), dim3(kThreads), 0, c.s, a);
+  else
+    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, bf16>), dim3((unsigned)blocks), dim3(kThreads), 0, c.s, a);
+  return hipGetLastError();
+}
+
+static hipError_t dw_any2(const Ctx& c, const DwArgs2& a) {
+  if (a.M % 256 == 0) return dw_launch<Tiling<256, 128, 2, 2>>(c, a);
+  return dw_launch<Tiling<128, 128, 2, 2>>(c, a);
+}
+
+hipError_t launch_dw2_bf16(const Ctx& c, const void* dos, const void* h, void* dw2) {
+  DwArgs2 a{c.counts, c.offsets, (const bf16*)dos, (const bf16*)h, dw2, c.H, c.I, c.H, c.I};
+  return dw_any2(c, a);
+}
+
+hipError_t launch_dw1_bf16(const Ctx& c, const void* dgu, const void* xs, void* dw1) {
+  DwArgs2 a{c.counts, c.offsets, (const bf16*)dgu, (const bf16*)xs, dw1, 2 * c.I, c.H, 2 * c.I, c.H};
+  return dw_any2(c, a);
+}
+
+}  // namespace mok

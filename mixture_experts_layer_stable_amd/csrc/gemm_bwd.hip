@@ -1,4 +1,5 @@
-// Backward grouped expert GEMMs.
+// Backward grouped expert GEMMs, fp32 path (bf16 runs on the direct-to-LDS
+// core in gemm2.hip).
 //
 // dH: pull reverse-combine -- dY rows gathered through the schedule's
 //   permutation into LDS -- times W2[e] (MN-contiguous, transposed in
@@ -7,9 +8,10 @@
 //   dothoosh.com MoK page, "Technical details of the MoK mechanism"):
 //     g'_partial(row, n-tile) = sum over the tile's columns of dA * h
 //     dh = g * dA;  da = dh*u*sig(a)*(1 + a*(1 - sig(a)));  du = dh*silu(a)
-//   Partials are summed in a fixed order -- a 32-lane butterfly per 32-column
-//   block, blocks in ascending column order, then N-tiles ascending in the
-//   router-backward kernel -- independent of the wave layout; no float atomics.
+//   Partials are summed in a fixed order -- 16 columns sequentially per lane,
+//   the two halves of each 32-column block, blocks in ascending column order,
+//   then N-tiles ascending in the router-backward kernel -- independent of the
+//   wave layout; no float atomics.
 // dX: push reverse-dispatch -- q = dGU . W1[e] written to the (token, slot)
 //   partial row perm[row]; reduced per token in slot order afterwards.
 // dW2[e] = sum_r (g*dY)_r^T h_r and dW1[e] = sum_r dGU_r^T x_r: K runs over the
@@ -78,36 +80,33 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs<T> a) {
     sb.src = DenseMN<T>{a.w2 + (int64_t)t.e * a.H * a.I + t.n * Tl::BN, a.I};
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop<T, Tl>(sa, sb, a.H / BKE, smem, wm, wn, lane, acc);
+    epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&dA)[16], const float (&)[16]) {
+      const bool ok = row < t.nrows;
+      float part = 0.0f;
+      if (ok) {
+        const int64_t R = t.row0 + row;
+        const int c = t.n * Tl::BN + col;
+        const float g = a.gate[s_slot[row]];
+        float av[16], uv[16], hv[16], da[16], du[16];
+        load16<T>(a.au + R * I2 + c, av);
+        load16<T>(a.au + R * I2 + a.I + c, uv);
+        load16<T>(a.h + R * a.I + c, hv);
 #pragma unroll
-    for (int fm = 0; fm < Tl::FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = acc_row<Tl>(wm, fm, r, lane);
-        const bool ok = i < t.nrows;
-        const int64_t R = t.row0 + i;
-        const float g = ok ? a.gate[s_slot[i]] : 0.0f;
-#pragma unroll
-        for (int fn = 0; fn < Tl::FN; ++fn) {
-          const int cl = acc_col<Tl>(wn, fn, lane);
-          const int c = t.n * Tl::BN + cl;
-          float part = 0.0f;
-          if (ok) {
-            const float dA = acc[fm][fn][r];
-            const float av = Elem<T>::get(a.au, R * I2 + c);
-            const float uv = Elem<T>::get(a.au, R * I2 + a.I + c);
-            part = dA * Elem<T>::get(a.h, R * a.I + c);
-            const float dh = g * dA;
-            const float sg = 1.0f / (1.0f + expf(-av));
-            Elem<T>::put(a.dgu, R * I2 + c, dh * uv * sg * (1.0f + av * (1.0f - sg)));
-            Elem<T>::put(a.dgu, R * I2 + a.I + c, dh * av * sg);
-          }
-          // sum over this 32-column block (fixed butterfly), one value per (block, row)
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) part += __shfl_xor(part, off);
-          if ((lane & 31) == 0) s_red[cl >> 5][i] = part;
+        for (int i = 0; i < 16; ++i) {
+          part = __builtin_fmaf(dA[i], hv[i], part);
+          const float dh = g * dA[i];
+          const float sg = 1.0f / (1.0f + expf(-av[i]));
+          da[i] = dh * uv[i] * sg * (1.0f + av[i] * (1.0f - sg));
+          du[i] = dh * av[i] * sg;
         }
+        store16<T>(a.dgu + R * I2 + c, da);
+        store16<T>(a.dgu + R * I2 + a.I + c, du);
       }
-    __syncthreads();
+      // the 32-column block's sum: columns 0-15 (even lane) + columns 16-31 (odd lane)
+      const float other = __shfl_xor(part, 1);
+      const float blk = (lane & 1) ? other + part : part + other;
+      if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+    });
     // blocks in ascending column order: the result depends on BN only, not on the wave layout
     for (int i = tid; i < t.nrows; i += kThreads) {
       float s = 0.0f;
@@ -142,18 +141,9 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs<T> a) {
     sb.src = DenseMN<T>{a.w1 + (int64_t)t.e * I2 * a.H + t.n * Tl::BN, a.H};
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop<T, Tl>(sa, sb, I2 / BKE, smem, wm, wn, lane, acc);
-#pragma unroll
-    for (int fm = 0; fm < Tl::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < Tl::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = acc_row<Tl>(wm, fm, r, lane);
-          if (i < t.nrows) {
-            const int64_t s = s_slot[i];
-            Elem<T>::put(a.part, s * a.H + t.n * Tl::BN + acc_col<Tl>(wn, fn, lane), acc[fm][fn][r]);
-          }
-        }
+    epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+      if (row < t.nrows) store16<T>(a.part + (int64_t)s_slot[row] * a.H + t.n * Tl::BN + col, g);
+    });
   });
 }
 
@@ -243,13 +233,9 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs<T, TO> a) {
     main_loop<T, Tl>(sa, sb, KT, smem, wm, wn, lane, acc);
   }
   TO* out = a.out + ((int64_t)e * M + mt * Tl::BM) * N + nt * Tl::BN;
-#pragma unroll
-  for (int fm = 0; fm < Tl::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < Tl::FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        Elem<TO>::put(out, (int64_t)acc_row<Tl>(wm, fm, r, lane) * N + acc_col<Tl>(wn, fn, lane), acc[fm][fn][r]);
+  epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+    store16<TO>(out + (int64_t)row * N + col, g);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -311,17 +297,15 @@ static hipError_t dx_bn(const Ctx& c, const void* dgu, const void* w1, void* par
 hipError_t launch_dh(const Ctx& c, const void* dy, const void* w2, const void* au, const void* h, const float* gate,
                      void* dgu, float* dgp) {
   if (c.R == 0) return hipSuccess;
-  const bool b256 = bn_rows(c.I) == 256;
-  if (c.act == MOK_F32)
-    return b256 ? dh_bn<float, 256>(c, dy, w2, au, h, gate, dgu, dgp) : dh_bn<float, 128>(c, dy, w2, au, h, gate, dgu, dgp);
-  return b256 ? dh_bn<bf16, 256>(c, dy, w2, au, h, gate, dgu, dgp) : dh_bn<bf16, 128>(c, dy, w2, au, h, gate, dgu, dgp);
+  if (c.act != MOK_F32) return launch_dh_bf16(c, dy, w2, au, h, gate, dgu, dgp);
+  return bn_rows(c.I) == 256 ? dh_bn<float, 256>(c, dy, w2, au, h, gate, dgu, dgp)
+                             : dh_bn<float, 128>(c, dy, w2, au, h, gate, dgu, dgp);
 }
 
 hipError_t launch_dx(const Ctx& c, const void* dgu, const void* w1, void* part) {
   if (c.R == 0) return hipSuccess;
-  const bool b256 = bn_rows(c.H) == 256;
-  if (c.act == MOK_F32) return b256 ? dx_bn<float, 256>(c, dgu, w1, part) : dx_bn<float, 128>(c, dgu, w1, part);
-  return b256 ? dx_bn<bf16, 256>(c, dgu, w1, part) : dx_bn<bf16, 128>(c, dgu, w1, part);
+  if (c.act != MOK_F32) return launch_dx_bf16(c, dgu, w1, part);
+  return bn_rows(c.H) == 256 ? dx_bn<float, 256>(c, dgu, w1, part) : dx_bn<float, 128>(c, dgu, w1, part);
 }
 
 template <typename T, typename TO, bool IS_DW2>
@@ -334,19 +318,13 @@ static hipError_t dw_t(const Ctx& c, const T* tok, const float* gate, const T* r
   return hipGetLastError();
 }
 
-template <bool IS_DW2>
-static hipError_t dw_any(const Ctx& c, const void* tok, const float* gate, const void* rows, void* out) {
-  if (c.act == MOK_F32) return dw_t<float, float, IS_DW2>(c, (const float*)tok, gate, (const float*)rows, out);
-  if (c.wgrad_f32) return dw_t<bf16, float, IS_DW2>(c, (const bf16*)tok, gate, (const bf16*)rows, out);
-  return dw_t<bf16, bf16, IS_DW2>(c, (const bf16*)tok, gate, (const bf16*)rows, out);
-}
-
+// fp32 weight gradients (bf16 runs on the direct-to-LDS core over pre-gathered rows)
 hipError_t launch_dw2(const Ctx& c, const void* dy, const float* gate, const void* h, void* dw2) {
-  return dw_any<true>(c, dy, gate, h, dw2);
+  return dw_t<float, float, true>(c, (const float*)dy, gate, (const float*)h, dw2);
 }
 
 hipError_t launch_dw1(const Ctx& c, const void* dgu, const void* x, void* dw1) {
-  return dw_any<false>(c, x, nullptr, dgu, dw1);
+  return dw_t<float, float, false>(c, (const float*)x, nullptr, (const float*)dgu, dw1);
 }
 
 }  // namespace mok

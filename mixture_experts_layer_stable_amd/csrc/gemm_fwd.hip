@@ -1,4 +1,5 @@
-// Forward grouped expert GEMMs.
+// Forward grouped expert GEMMs, fp32 path (bf16 runs on the direct-to-LDS
+// core in gemm2.hip).
 //
 // FC1 + SwiGLU: pull dispatch -- the A tile is gathered straight from x through
 // the schedule's permutation (token = perm[row] / k) into LDS; B is the
@@ -66,23 +67,19 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<T> a) {
     });
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop<T, Tl>(sa, sb, a.H / BKE, smem, wm, wn, lane, acc);
+    epilogue16<Tl, true>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&u)[16]) {
+      if (row >= t.nrows) return;
+      const int64_t R = t.row0 + row;
+      // tile column of a gate block -> gate column of W1: blocks alternate gate/up per wave
+      const int wj = col / Tl::WTN, cw = col % Tl::WTN;
+      const int c = cbase + wj * (Tl::WTN / 2) + (cw >> 6) * 32 + (cw & 31);
+      float hv[16];
 #pragma unroll
-    for (int fm = 0; fm < Tl::FM; ++fm)
-#pragma unroll
-      for (int p = 0; p < Tl::FN / 2; ++p)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = acc_row<Tl>(wm, fm, r, lane);
-          if (i < t.nrows) {
-            const int64_t R = t.row0 + i;
-            const int c = cbase + wn * (Tl::WTN / 2) + p * 32 + (lane & 31);
-            const float av = acc[fm][2 * p][r], uv = acc[fm][2 * p + 1][r];
-            const float hv = av / (1.0f + expf(-av)) * uv;
-            Elem<T>::put(a.au, R * I2 + c, av);
-            Elem<T>::put(a.au, R * I2 + a.I + c, uv);
-            Elem<T>::put(a.h, R * a.I + c, hv);
-          }
-        }
+      for (int i = 0; i < 16; ++i) hv[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+      store16<T>(a.au + R * I2 + c, g);
+      store16<T>(a.au + R * I2 + a.I + c, u);
+      store16<T>(a.h + R * a.I + c, hv);
+    });
   });
 }
 
@@ -109,18 +106,9 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args<T> a) {
     sb.L.init(tid, [&](int j) -> const T* { return a.w2 + ((int64_t)t.e * a.H + t.n * Tl::BN + j) * a.I; });
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop<T, Tl>(sa, sb, a.I / BKE, smem, wm, wn, lane, acc);
-#pragma unroll
-    for (int fm = 0; fm < Tl::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < Tl::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = acc_row<Tl>(wm, fm, r, lane);
-          if (i < t.nrows) {
-            const int64_t s = s_slot[i];
-            Elem<T>::put(a.part, s * a.H + t.n * Tl::BN + acc_col<Tl>(wn, fn, lane), acc[fm][fn][r]);
-          }
-        }
+    epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+      if (row < t.nrows) store16<T>(a.part + (int64_t)s_slot[row] * a.H + t.n * Tl::BN + col, g);
+    });
   });
 }
 
@@ -180,14 +168,13 @@ static hipError_t fc2_bn(const Ctx& c, const void* h, const void* w2, void* part
 
 hipError_t launch_fc1(const Ctx& c, const void* x, const void* w1, void* au, void* h) {
   if (c.R == 0) return hipSuccess;
-  return c.act == MOK_F32 ? fc1_t<float>(c, x, w1, au, h) : fc1_t<bf16>(c, x, w1, au, h);
+  return c.act == MOK_F32 ? fc1_t<float>(c, x, w1, au, h) : launch_fc1_bf16(c, x, w1, au, h);
 }
 
 hipError_t launch_fc2(const Ctx& c, const void* h, const void* w2, void* part) {
   if (c.R == 0) return hipSuccess;
-  const bool b256 = bn_rows(c.H) == 256;
-  if (c.act == MOK_F32) return b256 ? fc2_bn<float, 256>(c, h, w2, part) : fc2_bn<float, 128>(c, h, w2, part);
-  return b256 ? fc2_bn<bf16, 256>(c, h, w2, part) : fc2_bn<bf16, 128>(c, h, w2, part);
+  if (c.act != MOK_F32) return launch_fc2_bf16(c, h, w2, part);
+  return bn_rows(c.H) == 256 ? fc2_bn<float, 256>(c, h, w2, part) : fc2_bn<float, 128>(c, h, w2, part);
 }
 
 }  // namespace mok

@@ -44,6 +44,17 @@ hipError_t launch_dw2(const Ctx& c, const void* dy, const float* gate, const voi
 hipError_t launch_dw1(const Ctx& c, const void* dgu, const void* x, void* dw1);
 hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr);
 
+// bf16 grouped GEMMs on the direct-to-LDS core
+hipError_t launch_fc1_bf16(const Ctx& c, const void* x, const void* w1, void* au, void* h);
+hipError_t launch_fc2_bf16(const Ctx& c, const void* h, const void* w2, void* part);
+hipError_t launch_dh_bf16(const Ctx& c, const void* dy, const void* w2, const void* au, const void* h,
+                          const float* gate, void* dgu, float* dgp);
+hipError_t launch_dx_bf16(const Ctx& c, const void* dgu, const void* w1, void* part);
+hipError_t launch_dw2_bf16(const Ctx& c, const void* dos, const void* h, void* dw2);
+hipError_t launch_dw1_bf16(const Ctx& c, const void* dgu, const void* xs, void* dw1);
+// dst[r] = src[perm[r] / k] (times gate[perm[r]] when gate != nullptr), bf16 rows of H
+hipError_t launch_gather_rows(const Ctx& c, const void* src, const float* gate, void* dst);
+
 // Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
 inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }
 inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }

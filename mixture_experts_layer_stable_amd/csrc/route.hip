@@ -91,24 +91,24 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
     __syncthreads();
   }
 
-#pragma unroll 1
+#pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int64_t tok = t0 + wave * TPT + i;
-    if (tok >= Tn) break;
-    float v[EPT];
+    if (tok < Tn) {  // uniform across the wave
+      float v[EPT];
 #pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = acc[i][q];
-      if (bias != nullptr && e < E) v[q] = v[q] + bias[e];
-      if (logits != nullptr && e < E) logits[tok * E + e] = v[q];
-    }
-    uint32_t taken = 0;
-    float zsel[16];
-    int esel[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < k) {
+      for (int q = 0; q < EPT; ++q) {
+        const int e = lane + 64 * q;
+        v[q] = acc[i][q];
+        if (bias != nullptr && e < E) v[q] = v[q] + bias[e];
+        if (logits != nullptr && e < E) logits[tok * E + e] = v[q];
+      }
+      // k rounds of wave arg-max; lane j keeps slot j's expert and exp(z_j - z_0)
+      uint32_t taken = 0;
+      float z0 = 0.0f, s = 0.0f, my_ex = 0.0f;
+      int my_e = 0;
+#pragma unroll 1
+      for (int j = 0; j < k; ++j) {
         float bv = 0.0f;
         int be = kNoExpert;
 #pragma unroll
@@ -129,25 +129,17 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
           }
         }
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        zsel[j] = bv;
-        esel[j] = be;
+        if (j == 0) z0 = bv;
+        const float ex = expf(bv - z0);  // softmax over the selected logits, summed in slot order
+        s = s + ex;
+        if (lane == j) {
+          my_e = be;
+          my_ex = ex;
+        }
       }
-    }
-    // softmax over the selected logits, summed in slot order
-    float ex[16];
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < k) {
-        ex[j] = expf(zsel[j] - zsel[0]);
-        s = s + ex[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < k && lane == j) {
-        idx[tok * k + j] = esel[j];
-        gate[tok * k + j] = ex[j] / s;
+      if (lane < k) {
+        idx[tok * k + lane] = my_e;
+        gate[tok * k + lane] = my_ex / s;
       }
     }
   }
