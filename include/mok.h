@@ -68,7 +68,7 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
 
 /*
  * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;
- * H and I positive multiples of 128; T*k < 2^31.  act is MOK_F32 or MOK_BF16
+ * H and I positive multiples of 128; T*k, T*H, T*k*2I and 2I*H below 2^31.  act is MOK_F32 or MOK_BF16
  * and gemm must equal act (MOK_MXFP8 expert GEMMs are rejected with
  * MOK_ERR_DTYPE by this version).
  * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile

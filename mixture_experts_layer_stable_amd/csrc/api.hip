@@ -22,7 +22,10 @@ mok_status check_desc(const mok_desc* d) {
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > 16 || d->k > d->E) return MOK_ERR_SHAPE;
   if (d->H <= 0 || d->I <= 0 || d->H % 128 != 0 || d->I % 128 != 0) return MOK_ERR_SHAPE;
   if (d->T * (int64_t)d->k >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
-  if ((int64_t)d->I * 2 * d->H >= ((int64_t)1 << 31) / 2) return MOK_ERR_SHAPE;
+  // 32-bit byte offsets inside one operand: token rows, routed rows, one expert's weights
+  if (d->T * (int64_t)d->H >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
+  if (d->T * (int64_t)d->k * 2 * d->I >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
+  if ((int64_t)d->I * 2 * d->H >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
   if (d->tile_m != 0 && d->tile_m != 32 && d->tile_m != 64 && d->tile_m != 128) return MOK_ERR_SHAPE;
   if (d->grid < 0) return MOK_ERR_SHAPE;
   return MOK_OK;

@@ -152,7 +152,8 @@ struct MNLoader {
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tiling {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int NW = WM * WN;        // waves per workgroup
+  static constexpr int NT = 64 * NW;        // threads per workgroup
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -293,12 +294,12 @@ __device__ __forceinline__ void for_each_row_tile(const Sched& sc, const int* s_
     const int e = a;
     const int Me = s_ts[e + 1] - s_ts[e];
     const int rel = (int)(L - (int64_t)s_ts[e] * NTN);
-    RowTile t;
-    t.e = e;
-    t.n = rel / Me;
-    t.m = rel - t.n * Me;
-    t.row0 = sc.offsets[e] + t.m * sc.BM;
-    t.nrows = min(sc.BM, sc.counts[e] - t.m * sc.BM);
+    RowTile t;  // wave-uniform values: keep them in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.n = __builtin_amdgcn_readfirstlane(rel / Me);
+    t.m = __builtin_amdgcn_readfirstlane(rel - t.n * Me);
+    t.row0 = __builtin_amdgcn_readfirstlane(sc.offsets[t.e] + t.m * sc.BM);
+    t.nrows = __builtin_amdgcn_readfirstlane(min(sc.BM, sc.counts[t.e] - t.m * sc.BM));
     body(t);
   }
 }

@@ -55,88 +55,128 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz_mn(int k) { return 4 * (k & 3); }
 
+// DMA with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit offset:
+// advancing along K only changes the scalar base.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ void dma16_sv(const char* sbase, uint32_t voff, char* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint4 tr_pair(const char* a0, const char* a1) {
+  const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)a0);
+  const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)a1);
+  const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
+  return make_uint4(u0.x, u0.y, u1.x, u1.y);
+}
+
 // ---------------------------------------------------------------------------
-// K-contiguous operand, ROWS rows x 64 bf16 per stage.
+// K-contiguous operand, ROWS rows x 64 bf16 per stage; this wave reads NF
+// fragments (32-row blocks) per k-step. Sources are sbase + per-lane 32-bit
+// byte offsets (row offset + chunk), sbase advancing 128 bytes per K-tile.
 // ---------------------------------------------------------------------------
-template <int ROWS>
+template <int ROWS, int NF, int NW>
 struct OpK {
   static constexpr int BK = 64;
   static constexpr int BYTES = ROWS * 128;
-  static constexpr int NI = ROWS / 32;  // DMA instructions per wave per stage (8 rows each)
-  static_assert(ROWS % 32 == 0, "rows");
-  const char* src[NI];
+  static constexpr int NI = ROWS / (8 * NW);  // DMA instructions per wave per stage (8 rows each)
+  static_assert(ROWS % (8 * NW) == 0, "rows");
+  const char* sbase;
+  uint32_t voff[NI];
+  uint32_t foff[NF][4];
 
-  // rowptr(row) -> const bf16* at K offset 0; must be readable for the whole K range.
-  template <class F> __device__ __forceinline__ void init(int wave, int lane, F rowptr) {
+  // rowoff(row) -> byte offset of the row's K start from sbase_ (< 4 GiB);
+  // frow(f) -> first tile row of fragment f of this wave.
+  template <class F, class G>
+  __device__ __forceinline__ void init(const void* sbase_, F rowoff, G frow, int wave, int lane) {
+    sbase = reinterpret_cast<const char*>(sbase_);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int row = 8 * (wave + 4 * j) + (lane >> 3);
-      src[j] = reinterpret_cast<const char*>(rowptr(row)) + 16 * ((lane & 7) ^ swz_k(row));
+      const int row = 8 * (wave + NW * j) + (lane >> 3);
+      voff[j] = rowoff(row) + 16u * (uint32_t)((lane & 7) ^ swz_k(row));
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = frow(f) + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) foff[f][ks] = row * 128 + 16 * ((2 * ks + (lane >> 5)) ^ swz_k(row));
     }
   }
   __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
+    const char* b = uniform_ptr(sbase + (int64_t)kt * 128);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) dma16(src[j] + (int64_t)kt * 128, stage + (wave + 4 * j) * 1024);
+    for (int j = 0; j < NI; ++j) dma16_sv(b, voff[j], stage + (wave + NW * j) * 1024);
   }
-  __device__ __forceinline__ uint4 frag(const char* stage, int row0, int ks, int lane) const {
-    const int row = row0 + (lane & 31);
-    return *reinterpret_cast<const uint4*>(stage + row * 128 + 16 * ((2 * ks + (lane >> 5)) ^ swz_k(row)));
+  __device__ __forceinline__ uint4 frag(const char* stage, int f, int ks) const {
+    return *reinterpret_cast<const uint4*>(stage + foff[f][ks]);
   }
 };
 
 // ---------------------------------------------------------------------------
 // MN-contiguous operand, BK k-rows x ROWS bf16 per stage. Row k of the whole
-// operand starts at base + (k0 + k) * ld (bytes); rows k >= cnt read zeros.
+// operand starts at sbase + k * ld (bytes); rows k >= cnt read zeros (only the
+// last K-tile checks). NF fragments per k-step for this wave.
 // ---------------------------------------------------------------------------
-template <int ROWS, int BK_>
+template <int ROWS, int BK_, int NF, int NW>
 struct OpMN {
   static constexpr int BK = BK_;
   static constexpr int PITCH = ROWS * 2;
   static constexpr int BYTES = BK * PITCH;
-  static constexpr int NI = BYTES / 4096;      // per wave per stage
-  static constexpr int RPI = 1024 / PITCH;     // k-rows per DMA instruction
-  static_assert(BYTES % 4096 == 0 && PITCH <= 1024, "tile");
-  const char* base;  // byte address of row 0 at this lane's column chunk (before swizzle)
+  static constexpr int NI = BYTES / (1024 * NW);  // per wave per stage
+  static_assert(BYTES % (1024 * NW) == 0 && PITCH <= 1024, "tile");
+  const char* sbase;
   int64_t ld;
   int cnt;
-  int krow[NI];
-  int colb[NI];
+  uint32_t voff[NI];   // krow * ld + swizzled column chunk
+  uint32_t foff[NF];   // fragment (mb, ks = 0, first read) offset in the stage
 
-  __device__ __forceinline__ void init(const void* base_, int64_t ld_bytes, int cnt_, int wave, int lane) {
-    base = reinterpret_cast<const char*>(base_);
+  template <class G>
+  __device__ __forceinline__ void init(const void* base_, int64_t ld_bytes, int cnt_, G fcol, int wave, int lane) {
+    sbase = reinterpret_cast<const char*>(base_);
     ld = ld_bytes;
     cnt = cnt_;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int o = (wave + 4 * j) * 1024 + 16 * lane;  // byte position in the stage
-      krow[j] = o / PITCH;
-      colb[j] = 16 * (((o % PITCH) >> 4) ^ swz_mn(krow[j]));
+      const int o = (wave + NW * j) * 1024 + 16 * lane;  // byte position in the stage
+      const int kr = o / PITCH;
+      voff[j] = (uint32_t)(kr * ld_bytes) + 16u * (uint32_t)(((o % PITCH) >> 4) ^ swz_mn(kr));
+    }
+    const int g = lane >> 4, i = lane & 15;
+    const int k0 = 8 * (g >> 1) + (i >> 2);  // k-row of the first read at ks = 0; k0 & 3 = (i >> 2) & 3
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int mn = fcol(f) + 16 * (g & 1) + 4 * (i & 3);
+      foff[f] = k0 * PITCH + 16 * ((mn >> 3) ^ swz_mn(k0)) + 2 * (mn & 7);
     }
   }
   __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
+    const int k0 = kt * BK;
+    if (k0 + BK <= cnt) {
+      const char* b = uniform_ptr(sbase + (int64_t)k0 * ld);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int k = kt * BK + krow[j];
-      const char* p = k < cnt ? base + (int64_t)k * ld + colb[j] : reinterpret_cast<const char*>(g_zero_1k) + colb[j];
-      dma16(p, stage + (wave + 4 * j) * 1024);
+      for (int j = 0; j < NI; ++j) dma16_sv(b, voff[j], stage + (wave + NW * j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int o = (wave + NW * j) * 1024 + 16 * (threadIdx.x & 63);
+        const int kr = o / PITCH;
+        const uint32_t col = voff[j] - (uint32_t)(kr * ld);
+        const char* p = k0 + kr < cnt ? sbase + (int64_t)(k0 + kr) * ld + col
+                                      : reinterpret_cast<const char*>(g_zero_1k) + col;
+        dma16(p, stage + (wave + NW * j) * 1024);
+      }
     }
   }
-  // fragment for columns mb .. mb+31 and k-step ks (16 k) of the stage
-  __device__ __forceinline__ uint4 frag(const char* stage, int mb, int ks, int lane) const {
-    const int g = lane >> 4, i = lane & 15;
-    const int mn = mb + 16 * (g & 1) + 4 * (i & 3);
-    const int k0 = 16 * ks + 8 * (g >> 1) + (i >> 2);
-    const int k1 = k0 + 4;
-    const char* a0 = stage + k0 * PITCH + 16 * ((mn >> 3) ^ swz_mn(k0)) + 2 * (mn & 7);
-    const char* a1 = stage + k1 * PITCH + 16 * ((mn >> 3) ^ swz_mn(k1)) + 2 * (mn & 7);
-    const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)a0);
-    const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)a1);
-    uint4 v;
-    v.x = (uint16_t)r0[0] | ((uint32_t)(uint16_t)r0[1] << 16);
-    v.y = (uint16_t)r0[2] | ((uint32_t)(uint16_t)r0[3] << 16);
-    v.z = (uint16_t)r1[0] | ((uint32_t)(uint16_t)r1[1] << 16);
-    v.w = (uint16_t)r1[2] | ((uint32_t)(uint16_t)r1[3] << 16);
-    return v;
+  // k-step ks: rows 16ks + {k0, k0+4} relative to the first read
+  __device__ __forceinline__ uint4 frag(const char* stage, int f, int ks) const {
+    const char* a = stage + foff[f] + ks * 16 * PITCH;
+    return tr_pair(a, a + 4 * PITCH);
   }
 };
 
@@ -187,9 +227,9 @@ __device__ __forceinline__ void main_loop2(const OA& oa, const OB& ob, int KT, c
     for (int ks = 0; ks < KS; ++ks) {
       uint4 a[Tl::FM], b[Tl::FN];
 #pragma unroll
-      for (int fm = 0; fm < Tl::FM; ++fm) a[fm] = oa.frag(cur, wm * Tl::WTM + fm * 32, ks, lane);
+      for (int fm = 0; fm < Tl::FM; ++fm) a[fm] = oa.frag(cur, fm, ks);
 #pragma unroll
-      for (int fn = 0; fn < Tl::FN; ++fn) b[fn] = ob.frag(cur + OA::BYTES, wn * Tl::WTN + fn * 32, ks, lane);
+      for (int fn = 0; fn < Tl::FN; ++fn) b[fn] = ob.frag(cur + OA::BYTES, fn, ks);
 #pragma unroll
       for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll

@@ -25,10 +25,12 @@ __device__ uint4 g_zero_1k[64] = {};
 
 constexpr int kMaxE2 = 1024;
 constexpr int kRowStages = 3;
-constexpr int kDwStages = 3;
+constexpr int kDwStages = 4;
 
+// Row GEMM wave layouts: 8 waves (2 per SIMD, 64x64 or 32x64 wave tiles) for
+// 64- and 128-row tiles; 4 waves for 32-row tiles (keeps gate/up block pairs).
 template <int BM, int BN>
-using RowTiling2 = Tiling<BM, BN, (BM == 128 ? 2 : 1), (BM == 128 ? 2 : 4)>;
+using RowTiling2 = Tiling<BM, BN, (BM == 32 ? 1 : 2), (BM == 32 ? 4 : 4)>;
 
 struct RowArgs {
   Sched sc;
@@ -46,10 +48,10 @@ struct RowArgs {
 enum RowKind { FC1 = 0, FC2 = 1, DH = 2, DX = 3 };
 
 template <int KIND, class Tl>
-__global__ __launch_bounds__(256) void row_gemm2_kernel(RowArgs a) {
-  using OA = OpK<Tl::BM>;
+__global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
+  using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
   constexpr bool B_MN = KIND == DH || KIND == DX;
-  using OB = typename std::conditional<B_MN, OpMN<Tl::BN, 64>, OpK<Tl::BN>>::type;
+  using OB = typename std::conditional<B_MN, OpMN<Tl::BN, 64, Tl::FN, Tl::NW>, OpK<Tl::BN, Tl::FN, Tl::NW>>::type;
   constexpr int SB = OA::BYTES + OB::BYTES;
   __shared__ __align__(1024) char smem[kRowStages * SB];
   __shared__ int s_ts[kMaxE2 + 1];
@@ -64,29 +66,37 @@ __global__ __launch_bounds__(256) void row_gemm2_kernel(RowArgs a) {
   load_tile_start(a.sc, s_ts);
   for_each_row_tile(a.sc, s_ts, N / Tl::BN, [&](const RowTile& t) {
     __syncthreads();
-    for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
+    for (int i = tid; i < Tl::BM; i += Tl::NT) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();
+    const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
+    const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
     OA oa;
-    oa.init(wave, lane, [&](int row) -> const bf16* {
-      const int r = row < t.nrows ? row : 0;  // padding rows re-read row 0 (finite; their outputs are dropped)
-      if constexpr (KIND == FC1 || KIND == DH) return a.a + (int64_t)(s_slot[r] / a.k) * a.H;
-      else return a.a + (int64_t)(t.row0 + r) * K;
-    });
+    if constexpr (KIND == FC1 || KIND == DH) {
+      // gathered token rows; padding rows re-read row 0 (finite; their outputs are dropped)
+      oa.init(a.a, [&](int row) -> uint32_t {
+        return (uint32_t)(s_slot[row < t.nrows ? row : 0] / a.k) * (uint32_t)(2 * a.H);
+      }, frow_a, wave, lane);
+    } else {
+      oa.init(a.a + (int64_t)t.row0 * K, [&](int row) -> uint32_t {
+        return (uint32_t)(row < t.nrows ? row : 0) * (uint32_t)(2 * K);
+      }, frow_a, wave, lane);
+    }
     OB ob;
     if constexpr (B_MN) {
       // dh: W2[e] [H][I], k = h, columns i; dx: W1[e] [2I][H], k = c, columns h
       const bf16* base = KIND == DH ? a.w + (int64_t)t.e * a.H * a.I + t.n * Tl::BN
                                     : a.w + (int64_t)t.e * I2 * a.H + t.n * Tl::BN;
-      ob.init(base, 2 * (int64_t)(KIND == DH ? a.I : a.H), K, wave, lane);
+      ob.init(base, 2 * (int64_t)(KIND == DH ? a.I : a.H), K, frow_b, wave, lane);
     } else if constexpr (KIND == FC1) {
       const int cbase = t.n * (Tl::BN / 2);
-      ob.init(wave, lane, [&](int j) -> const bf16* {
+      ob.init(a.w + (int64_t)t.e * I2 * a.H, [&](int j) -> uint32_t {
         const int wj = j / Tl::WTN, fn = (j % Tl::WTN) >> 5;
         const int c = cbase + wj * (Tl::WTN / 2) + (fn >> 1) * 32 + (j & 31);
-        return a.w + ((int64_t)t.e * I2 + ((fn & 1) ? a.I + c : c)) * a.H;
-      });
+        return (uint32_t)((fn & 1) ? a.I + c : c) * (uint32_t)(2 * a.H);
+      }, frow_b, wave, lane);
     } else {
-      ob.init(wave, lane, [&](int j) -> const bf16* { return a.w + ((int64_t)t.e * a.H + t.n * Tl::BN + j) * a.I; });
+      ob.init(a.w + ((int64_t)t.e * a.H + t.n * Tl::BN) * a.I,
+              [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)(2 * a.I); }, frow_b, wave, lane);
     }
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop2<Tl, kRowStages>(oa, ob, K / 64, smem, wave, wm, wn, lane, acc);
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(256) void row_gemm2_kernel(RowArgs a) {
         const float blk = (lane & 1) ? other + part : part + other;
         if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
       });
-      for (int i = tid; i < t.nrows; i += kThreads) {
+      for (int i = tid; i < t.nrows; i += Tl::NT) {
         float s = 0.0f;
 #pragma unroll
         for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
@@ -159,9 +169,9 @@ struct DwArgs2 {
 };
 
 template <class Tl, typename TO>
-__global__ __launch_bounds__(256) void dw_gemm2_kernel(DwArgs2 a) {
-  using OA = OpMN<Tl::BM, 32>;
-  using OB = OpMN<Tl::BN, 32>;
+__global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
+  using OA = OpMN<Tl::BM, 32, Tl::FM, Tl::NW>;
+  using OB = OpMN<Tl::BN, 32, Tl::FN, Tl::NW>;
   __shared__ __align__(1024) char smem[kDwStages * (OA::BYTES + OB::BYTES)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
@@ -172,9 +182,11 @@ __global__ __launch_bounds__(256) void dw_gemm2_kernel(DwArgs2 a) {
   const int mt = rem / NT, nt = rem - mt * NT;
   const int seg0 = a.offsets[e], cnt = a.counts[e];
   OA oa;
-  oa.init(a.arows + (int64_t)seg0 * a.lda + mt * Tl::BM, 2 * (int64_t)a.lda, cnt, wave, lane);
+  oa.init(a.arows + (int64_t)seg0 * a.lda + mt * Tl::BM, 2 * (int64_t)a.lda, cnt,
+          [&](int f) { return wm * Tl::WTM + f * 32; }, wave, lane);
   OB ob;
-  ob.init(a.brows + (int64_t)seg0 * a.ldb + nt * Tl::BN, 2 * (int64_t)a.ldb, cnt, wave, lane);
+  ob.init(a.brows + (int64_t)seg0 * a.ldb + nt * Tl::BN, 2 * (int64_t)a.ldb, cnt,
+          [&](int f) { return wn * Tl::WTN + f * 32; }, wave, lane);
   f32x16_t acc[Tl::FM][Tl::FN];
   main_loop2<Tl, kDwStages>(oa, ob, (cnt + 31) / 32, smem, wave, wm, wn, lane, acc);
   TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
@@ -192,7 +204,7 @@ static hipError_t row_launch(const Ctx& c, const RowArgs& a, int N) {
   int g = c.grid > 0 ? c.grid : c.num_cu;
   const int64_t upper = (int64_t)c.max_tiles * (N / BN);
   if (g > upper) g = (int)std::max<int64_t>(upper, 1);
-  hipLaunchKernelGGL((row_gemm2_kernel<KIND, Tl>), dim3(g), dim3(kThreads), 0, c.s, a);
+  hipLaunchKernelGGL((row_gemm2_kernel<KIND, Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a);
   return hipGetLastError();
 }
 
@@ -258,14 +270,14 @@ template <class Tl>
 static hipError_t dw_launch(const Ctx& c, const DwArgs2& a) {
   const int64_t blocks = (int64_t)c.E * (a.M / Tl::BM) * (a.N / Tl::BN);
   if (c.wgrad_f32)
-    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, float>), dim3((unsigned)blocks), dim3(kThreads), 0, c.s, a);
+    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
   else
-    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, bf16>), dim3((unsigned)blocks), dim3(kThreads), 0, c.s, a);
+    hipLaunchKernelGGL((dw_gemm2_kernel<Tl, bf16>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
   return hipGetLastError();
 }
 
 static hipError_t dw_any2(const Ctx& c, const DwArgs2& a) {
-  if (a.M % 256 == 0) return dw_launch<Tiling<256, 128, 2, 2>>(c, a);
+  if (a.M % 256 == 0 && a.N % 256 == 0) return dw_launch<Tiling<256, 256, 2, 4>>(c, a);
   return dw_launch<Tiling<128, 128, 2, 2>>(c, a);
 }
 
