@@ -223,17 +223,25 @@ __device__ __forceinline__ void main_loop2(const OA& oa, const OB& ob, int KT, c
       ob.issue(nk, st + OA::BYTES, wave);
     }
     const char* cur = smem + (kt % STAGES) * SB;
+    // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
+    uint4 a[2][Tl::FM], b[2][Tl::FN];
+#pragma unroll
+    for (int fm = 0; fm < Tl::FM; ++fm) a[0][fm] = oa.frag(cur, fm, 0);
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; ++fn) b[0][fn] = ob.frag(cur + OA::BYTES, fn, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 a[Tl::FM], b[Tl::FN];
+      const int c = ks & 1;
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int fm = 0; fm < Tl::FM; ++fm) a[fm] = oa.frag(cur, fm, ks);
+        for (int fm = 0; fm < Tl::FM; ++fm) a[c ^ 1][fm] = oa.frag(cur, fm, ks + 1);
 #pragma unroll
-      for (int fn = 0; fn < Tl::FN; ++fn) b[fn] = ob.frag(cur + OA::BYTES, fn, ks);
+        for (int fn = 0; fn < Tl::FN; ++fn) b[c ^ 1][fn] = ob.frag(cur + OA::BYTES, fn, ks + 1);
+      }
 #pragma unroll
       for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < Tl::FN; ++fn) Mma<bf16>::run(acc[fm][fn], a[fm], b[fn]);
+        for (int fn = 0; fn < Tl::FN; ++fn) Mma<bf16>::run(acc[fm][fn], a[c][fm], b[c][fn]);
     }
   }
   __syncthreads();

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
   __shared__ int s_ts[kMaxE2 + 1];
   __shared__ int s_slot[Tl::BM];
   __shared__ float s_red[KIND == DH ? Tl::BN / 32 : 1][KIND == DH ? Tl::BM : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
   // N of the GEMM and its tile count; K
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
   using OA = OpMN<Tl::BM, 32, Tl::FM, Tl::NW>;
   using OB = OpMN<Tl::BN, 32, Tl::FN, Tl::NW>;
   __shared__ __align__(1024) char smem[kDwStages * (OA::BYTES + OB::BYTES)];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
   const int L = xcd_logical(blockIdx.x, gridDim.x);
