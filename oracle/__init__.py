@@ -18,8 +18,11 @@ Sources (the pages describing Mixture-of-Kittens):
     (same inputs give the same outputs).
   * aikraft.ru MoK article, section 04: pull dispatch, push combine.
 
+MXFP8 quantisation and the MXFP8 step are in ``oracle.mx``.
+
 Every function is pinned by tests in tests/test_oracle_*.py against closed
 forms, brute force, torch.autograd on a dense formulation, and finite
 differences (see the docstrings of those tests).
 """
 from .moe import *  # noqa: F401,F403
+from . import mx  # noqa: F401

@@ -1,0 +1,178 @@
+"""Oracle MXFP8 quantisation and the MXFP8 layer step. TEST INFRASTRUCTURE ONLY.
+
+The expert GEMMs run on MXFP8 operands (dothoosh.com MoK page, "Technical details of the
+MoK mechanism": the megakernel supports BF16 and MXFP8). Format, from the OCP Microscaling
+(MX) specification v1.0: blocks of 32 consecutive elements along the GEMM's K share one
+E8M0 scale 2^s; elements are FP8 E4M3 (max normal 448, subnormals down to 2^-9).
+
+Quantisation of one block (values v, all exactly representable in bf16/fp32):
+  amax = max |v|;  if amax == 0: s = -127 and every element is 0;
+  else s = floor(log2 amax) - 8 (8 = exponent of E4M3's largest normal), clamped to
+  [-127, 127]; element = E4M3 round-to-nearest-even of v / 2^s, saturated to +-448.
+Dequantisation is exact: element * 2^s.
+
+Quantisation points of the step (each GEMM operand along that GEMM's K):
+  fc1  x rows along H,  W1 rows along H
+  fc2  h rows (bf16 as stored) along I,  W2 rows along I
+  dh   dY rows along H,  W2^T rows (columns of W2) along H
+  dx   dGU rows (bf16 as stored) along 2I,  W1^T rows along 2I
+  dw2  dO = bf16(g*dY) and h along tokens
+  dw1  dGU and x along tokens
+For the weight gradients, token blocks start at each expert's first row within each
+micro-batch and the last block of a segment is padded with zeros. The gate gradient is
+g' = <dA, h> with dA the dh GEMM result (the fused SonicMoE-style form; with quantised
+operands it is the method's definition).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .moe import bf16_round, round_to, sigmoid, silu, _slots_by_expert
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_round(v):
+    """Round-to-nearest-even onto FP8 E4M3 (3 mantissa bits, min normal 2^-6, subnormal
+    step 2^-9), saturating at +-448."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                                   # a = m * 2^e, 0.5 <= m < 1
+    q = np.exp2(np.maximum(e - 1, -6).astype(np.float64) - 3)
+    r = np.rint(v / q) * q
+    return np.clip(np.where(a == 0, 0.0 * v, r), -E4M3_MAX, E4M3_MAX)
+
+
+def mx_quantize(v, axis=-1):
+    """Blocks of 32 along `axis` (its length must be a multiple of 32).
+    Returns (elements as float64 E4M3 values, scale exponents s as int, same shape with
+    the axis divided by 32)."""
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    K = v.shape[-1]
+    assert K % MX_BLOCK == 0, K
+    blk = v.reshape(v.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blk).max(axis=-1)
+    _, e = np.frexp(amax)
+    s = np.clip(e - 1 - 8, -127, 127)
+    s = np.where(amax == 0, -127, s).astype(np.int64)
+    el = e4m3_round(blk / np.exp2(s.astype(np.float64))[..., None])
+    el = np.where((amax == 0)[..., None], 0.0, el)
+    return np.moveaxis(el.reshape(v.shape), -1, axis), np.moveaxis(s, -1, axis)
+
+
+def mx_dequantize(el, s, axis=-1):
+    el = np.moveaxis(np.asarray(el, np.float64), axis, -1)
+    s = np.moveaxis(np.asarray(s), axis, -1)
+    K = el.shape[-1]
+    out = el.reshape(el.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)) * np.exp2(s.astype(np.float64))[..., None]
+    return np.moveaxis(out.reshape(el.shape), -1, axis)
+
+
+def mx(v, axis=-1):
+    """Quantise then dequantise (the value a MXFP8 GEMM operand stands for)."""
+    return mx_dequantize(*mx_quantize(v, axis), axis=axis)
+
+
+def mx_token_blocks(rows, seg_lengths):
+    """Quantise token-major rows [n, F] along tokens, blocks of 32 starting at each
+    segment's first row, zero-padded at each segment's end; returns the dequantised
+    rows (same shape)."""
+    out = np.empty_like(np.asarray(rows, np.float64))
+    pos = 0
+    for n in seg_lengths:
+        if n == 0:
+            continue
+        pad = -(-n // MX_BLOCK) * MX_BLOCK
+        blk = np.zeros((pad, rows.shape[1]))
+        blk[:n] = rows[pos:pos + n]
+        out[pos:pos + n] = mx(blk, axis=0)[:n]
+        pos += n
+    return out
+
+
+def forward_mx(x, weights, idx, gate, E: int, I: int) -> dict:
+    """MXFP8 expert GEMMs, bf16 storage: same outputs as moe.forward(fmt='bf16') with
+    every GEMM operand quantised along its K."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    k = idx.shape[1]
+    R = T * k
+    a_s = np.full((R, I), np.nan)
+    u_s = np.full((R, I), np.nan)
+    h_s = np.full((R, I), np.nan)
+    p = np.full((R, H), np.nan)
+    for e, s in enumerate(_slots_by_expert(idx, E)):
+        if s.size == 0:
+            continue
+        X = mx(x[s // k])
+        W1 = mx(weights.w1(e))
+        A = X @ W1[:I].T
+        U = X @ W1[I:].T
+        Hh = bf16_round(silu(A) * U)
+        O = mx(Hh) @ mx(weights.w2(e)).T
+        a_s[s], u_s[s], h_s[s], p[s] = bf16_round(A), bf16_round(U), Hh, bf16_round(O)
+    g = np.asarray(gate, np.float64)
+    y = np.zeros((T, H))
+    for j in range(k):
+        y = y + g[:, j:j + 1] * p[j::k]
+    return dict(a=a_s, u=u_s, h=h_s, p=p, y=bf16_round(y))
+
+
+def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True) -> dict:
+    """Gradients with MXFP8 expert GEMMs. `segments[e]` lists the lengths of expert e's
+    row segments in slot order (one per micro-batch; default: one segment)."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    g = np.asarray(gate, np.float64)
+    T, H = x.shape
+    k = idx.shape[1]
+    E = np.asarray(wr).shape[0]
+    R = T * k
+    gf = g.ravel()
+    gp = np.full(R, np.nan)
+    dgu = np.full((R, 2 * I), np.nan)
+    q = np.full((R, H), np.nan)
+    dw1, dw2 = {}, {}
+    by_e = _slots_by_expert(idx, E)
+    for e, s in enumerate(by_e):
+        if s.size == 0:
+            dw1[e], dw2[e] = np.zeros((2 * I, H)), np.zeros((H, I))
+            continue
+        t = s // k
+        W1 = weights.w1(e)
+        W2 = weights.w2(e)
+        dA = mx(dy[t]) @ mx(W2, axis=0)                  # W2^T rows (columns of W2) along H
+        hh = fwd["h"][s]
+        gp[s] = np.einsum("ri,ri->r", dA, hh)
+        dh = gf[s][:, None] * dA
+        a, u = fwd["a"][s], fwd["u"][s]
+        sg = sigmoid(a)
+        G = bf16_round(np.concatenate([dh * u * sg * (1.0 + a * (1.0 - sg)), dh * (a * sg)], axis=1))
+        dgu[s] = G
+        q[s] = bf16_round(mx(G) @ mx(W1, axis=0))        # W1^T rows along 2I
+        seg = [s.size] if segments is None else segments[e]
+        dO = bf16_round(gf[s][:, None] * dy[t])
+        dw2[e] = bf16_round(mx_token_blocks(dO, seg).T @ mx_token_blocks(hh, seg))
+        dw1[e] = bf16_round(mx_token_blocks(G, seg).T @ mx_token_blocks(x[t], seg))
+    gpk = gp.reshape(T, k)
+    ssum = np.zeros(T)
+    for j in range(k):
+        ssum = ssum + g[:, j] * gpk[:, j]
+    dz = g * (gpk - ssum[:, None])
+    acc = np.zeros((T, H))
+    for j in range(k):
+        acc = acc + q[j::k]
+    out = dict(dgate=gpk, dz=dz, dgu=dgu, dw1=dw1, dw2=dw2, q=q)
+    if router:
+        wr64 = np.asarray(wr, np.float64)
+        for j in range(k):
+            acc = acc + dz[:, j:j + 1] * wr64[idx[:, j]]
+        dwr = np.zeros((E, H))
+        dzf = dz.ravel()
+        for e, s in enumerate(by_e):
+            if s.size:
+                dwr[e] = dzf[s] @ x[s // k]
+        out["dwr"] = bf16_round(dwr)
+    out["dx"] = bf16_round(acc)
+    return out
