@@ -31,6 +31,18 @@
  *  - Activation dtype `act` (MOK_F32 or MOK_BF16) is the storage type of
  *    x, y, dy, dx, the router weight wr, the expert weights and every saved or
  *    intermediate activation.  All arithmetic accumulates in fp32.
+ *  - Expert-GEMM dtype `gemm`: equal to `act`, or MOK_MXFP8 (with act = MOK_BF16):
+ *    every operand of the six expert GEMMs is then quantised to MXFP8 along that
+ *    GEMM's K (OCP Microscaling v1.0: FP8 E4M3 elements, round to nearest even,
+ *    saturating at +-448; one E8M0 scale 2^s per 32 elements, s = floor(log2 of
+ *    the block's largest magnitude) - 8 clamped to [-127, 127], stored as the byte
+ *    s + 127; an all-zero block has s = -127).  Quantised:
+ *      fc1  x rows and W1 rows along H;     fc2  h rows and W2 rows along I;
+ *      dh   dY rows and W2^T rows along H;  dx   dGU rows and W1^T rows along 2I;
+ *      dW2  dO = g*dY and h along routed rows;  dW1  dGU and x along routed rows,
+ *    the routed rows of one expert in blocks of 32 from its first row of the
+ *    whole step (all micro-batches, in token order), the last block zero-padded.
+ *    Quantiser inputs are the stored bf16 values; outputs are stored as with bf16.
  *  - Layouts: x, y, dy, dx [T][H]; wr [E][H]; w1 [E][2I][H] (rows 0..I-1 are
  *    the SwiGLU gate projection, rows I..2I-1 the up projection); w2 [E][H][I];
  *    idx [T][k] int32; gate, dgate, logits [T][k] / [T][E] fp32.
@@ -64,19 +76,30 @@ typedef enum mok_status {
 typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
 
 /* flags */
-#define MOK_FLAG_WGRAD_F32 1u /* dw1, dw2, dwr are written as fp32 instead of `act` */
+#define MOK_FLAG_WGRAD_F32 1u   /* dw1, dw2, dwr are written as fp32 instead of `act` */
+#define MOK_FLAG_WGRAD_DEFER 2u /* MXFP8 backward: stash this micro-batch's weight-gradient
+                                   operands only; dw1, dw2, dwr are not touched (see
+                                   mok_moe_backward) */
 
 /*
  * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;
- * H and I positive multiples of 128; T*k, T*H, T*k*2I and 2I*H below 2^31.  act is MOK_F32 or MOK_BF16
- * and gemm must equal act (MOK_MXFP8 expert GEMMs are rejected with
- * MOK_ERR_DTYPE by this version).
+ * H and I positive multiples of 128; T*k, T*H, T*k*2I and 2I*H below 2^31.
+ * act is MOK_F32 or MOK_BF16; gemm equals act, or is MOK_MXFP8 with act = MOK_BF16
+ * (anything else: MOK_ERR_DTYPE).
  * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile
  *   that still gives every grouped GEMM at least two full waves of the
  *   GPU's compute units.
  * grid: workgroups of the persistent GEMM kernels; 0 = one wave of the GPU.
+ * Micro-batch streaming (MXFP8 only; bf16/fp32 need mb_count <= 1): one step is
+ *   mb_count micro-batches of T tokens each, forward in any order and backward in
+ *   any order, every call naming its micro-batch in mb_index (0 <= mb_index <
+ *   mb_count).  ring: number of slots of the forward and backward workspaces
+ *   (the fixed ring that the pages' rotating token buffer becomes on one GPU);
+ *   micro-batch m uses slot m % ring, so calls for micro-batches in the same slot
+ *   must not overlap in time (one stream orders them).  mb_count = 0 and ring = 0
+ *   mean 1.  Extra limit for MXFP8: (mb_count*T*k + 128*E) * max(H, 2I) < 2^31.
  * The same descriptor must be passed to mok_schedule_build and to the
- * forward/backward calls that use that schedule.
+ * forward/backward calls that use that schedule (mb_index may differ).
  */
 typedef struct mok_desc {
   int64_t T;
@@ -86,22 +109,44 @@ typedef struct mok_desc {
   uint32_t flags;
   int32_t tile_m;
   int32_t grid;
-  int32_t reserved;
+  int32_t mb_index;
+  int32_t mb_count;
+  int32_t ring;
+  int32_t reserved; /* must be 0 */
 } mok_desc;
 
-/* Expert weights (device pointers, `act` dtype). */
+/* MXFP8 expert weights, quantised once per weight update by mok_weights_quantize.
+ * Each orientation is K-contiguous for the GEMM that reads it; *q are E4M3 bytes,
+ * *s the E8M0 scale bytes of consecutive 32-element blocks along K.
+ *   w1q  [E][2I][H],  w1s  [E][2I][H/32]   fc1 (K = H)
+ *   w2q  [E][H][I],   w2s  [E][H][I/32]    fc2 (K = I)
+ *   w2tq [E][I][H],   w2ts [E][I][H/32]    dh  (W2 transposed, K = H)
+ *   w1tq [E][H][2I],  w1ts [E][H][2I/32]   dx  (W1 transposed, K = 2I) */
+typedef struct mok_mx_weights {
+  void *w1q, *w1s, *w2q, *w2s, *w2tq, *w2ts, *w1tq, *w1ts;
+} mok_mx_weights;
+
+/* Expert weights (device pointers).  w1, w2 in `act`; mx (read only by the
+ * forward and backward calls) is required when gemm = MOK_MXFP8, else ignored. */
 typedef struct mok_weights {
-  const void* w1; /* [E][2I][H] */
-  const void* w2; /* [E][H][I]  */
+  const void* w1;            /* [E][2I][H] */
+  const void* w2;            /* [E][H][I]  */
+  const mok_mx_weights* mx;  /* host pointer to the MXFP8 orientations, or NULL */
 } mok_weights;
 
 /* Sizes in bytes of the caller-owned buffers (worst case over routings). */
 typedef struct mok_sizes {
   size_t sched;  /* schedule table (mok_schedule_build)                        */
-  size_t saved;  /* forward activations kept for the backward pass              */
-  size_t fwd_ws; /* forward scratch: per-(token,slot) partial rows [R][H]       */
+  size_t saved;  /* forward activations kept for the backward pass (per micro-batch) */
+  size_t fwd_ws; /* forward scratch: per-(token,slot) partial rows [R][H]; MXFP8:
+                    `ring` slots of partial rows and quantised x and h rows */
   size_t bwd_ws; /* backward scratch: dGU [R][2I], partials [R][H], d-gate parts,
-                    and for bf16 the routed-order rows of x and g*dy [R][H] each */
+                    and for bf16 the routed-order rows of x and g*dy [R][H] each.
+                    MXFP8: `ring` slots of quantised dY and dGU rows, partials and
+                    d-gate parts, then the weight-gradient stash of all mb_count
+                    micro-batches (routed-order x, g*dy, h, dGU rows, dz, counts)
+                    and the token-axis quantised operands of the dW GEMMs. The same
+                    bwd_ws must be passed to every backward call of one step. */
 } mok_sizes;
 
 /* Byte offsets of the schedule table's parts inside the schedule buffer.
@@ -165,6 +210,9 @@ mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched
  *   h = silu(a)*u, o = W2[e].h  -> partial row s (rounded to `act`),
  *   y_t = sum_{j=0..k-1} gate[t][j] * partial[t*k+j]   (fp32, slot order).
  * Writes y [T][H], saved (mok_saved_layout), uses ws (mok_sizes.fwd_ws).
+ * MXFP8: x rows and h rows are quantised along K inside the call (h in the fc1
+ * epilogue, from its bf16 value); w->mx supplies w1q/w1s and w2q/w2s.  Each
+ * micro-batch needs its own `saved` buffer until its backward call.
  */
 mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, const float* gate,
                            const mok_weights* w, void* y, void* saved, void* ws, void* stream);
@@ -184,6 +232,16 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
  * holds only the expert term.  dgate [T][k] fp32 receives g'.  Every element
  * of dw1 [E][2I][H], dw2 [E][H][I], dwr [E][H] is written (zero for experts
  * without tokens).  ws has mok_sizes.bwd_ws bytes.
+ * MXFP8 (gemm = MOK_MXFP8): dY rows are quantised along H and dGU rows along 2I
+ * inside the call (dGU in the dh epilogue); w->mx supplies w2tq/w2ts and
+ * w1tq/w1ts.  The weight gradients are deferred: every call copies micro-batch
+ * mb_index's routed-order x, dO = g*dy (rounded to bf16), h and dGU rows, its dz
+ * and its expert counts into the stash inside ws.  A call without
+ * MOK_FLAG_WGRAD_DEFER then computes dW1, dW2 (and dWr when dwr != NULL) over the
+ * stashed rows of all mb_count micro-batches -- each expert's rows in micro-batch
+ * order, which is token order -- so the result equals that of one call over the
+ * whole step; every micro-batch must have been stashed by a call since the
+ * previous such call.  With MOK_FLAG_WGRAD_DEFER, dw1/dw2/dwr may be NULL.
  */
 mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x, const int32_t* idx,
                             const float* gate, const mok_weights* w, const void* wr, const void* saved,
@@ -194,13 +252,26 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
  * Measurement aid (process-wide state, not thread-safe). While set, every
  * launch of the kernel group `name` -- one of "route", "schedule", "fc1",
  * "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "gather", "dw2",
- * "dw1", "dwr", or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
+ * "dw1", "dwr", and for MXFP8 "quant" (row quantisers and stash copies),
+ * "flush" (block table and token-axis quantisers), or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
  * and hipEventRecord(events[2n+1]) after it on the launch stream, for
  * n = 0, 1, ... < capacity; later launches are not bracketed.  `events` are
  * caller-created hipEvent_t handles.  name == NULL ends tracing.  The trace
  * never synchronises; elapsed times are read by the caller.
  */
 mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity);
+/*
+ * mok_weights_quantize -- the MXFP8 orientations of bf16 expert weights w1
+ * [E][2I][H] and w2 [E][H][I] (see mok_mx_weights for shapes): w1q/w2q quantise
+ * rows along their contiguous axis; w2tq[e][i][h] and w1tq[e][h][c] are W2[e][h][i]
+ * and W1[e][c][h] quantised in blocks of 32 along h and c respectively and stored
+ * transposed.  Requires act = MOK_BF16 and gemm = MOK_MXFP8; every pointer in
+ * *out non-NULL and 16-byte aligned.  Run once per weight update, outside the
+ * layer step.
+ */
+mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w2, const mok_mx_weights* out,
+                                void* stream);
+
 /* Launches bracketed since the last mok_trace_set. */
 int32_t mok_trace_count(void);
 /* Kernel group of the n-th bracketed launch (static string), or NULL. */

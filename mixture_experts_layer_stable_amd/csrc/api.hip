@@ -15,10 +15,25 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_size(int act) { return act == MOK_F32 ? 4 : 2; }
 
+int mb_count_of(const mok_desc* d) { return d->mb_count > 0 ? d->mb_count : 1; }
+int ring_of(const mok_desc* d) { return d->ring > 0 ? d->ring : 1; }
+bool is_mx(const mok_desc* d) { return d->gemm == MOK_MXFP8; }
+
+// Rows of the token-axis operands of the MXFP8 weight-gradient GEMMs: every
+// expert's rows of the step padded to a multiple of 128.
+int64_t mx_kmax(const mok_desc* d) {
+  return ((int64_t)mb_count_of(d) * d->T * d->k + 128LL * d->E + 127) / 128 * 128;
+}
+
 mok_status check_desc(const mok_desc* d) {
   if (d == nullptr) return MOK_ERR_NULL;
   if (d->act != MOK_F32 && d->act != MOK_BF16) return MOK_ERR_DTYPE;
-  if (d->gemm != d->act) return MOK_ERR_DTYPE;
+  if (d->gemm != d->act && !(d->gemm == MOK_MXFP8 && d->act == MOK_BF16)) return MOK_ERR_DTYPE;
+  if ((d->flags & MOK_FLAG_WGRAD_DEFER) && !is_mx(d)) return MOK_ERR_DTYPE;
+  if (d->reserved != 0 || d->mb_count < 0 || d->ring < 0 || d->mb_count > 1024 || d->ring > 1024)
+    return MOK_ERR_SHAPE;
+  if (d->mb_index < 0 || d->mb_index >= mb_count_of(d)) return MOK_ERR_SHAPE;
+  if (!is_mx(d) && mb_count_of(d) > 1) return MOK_ERR_SHAPE;
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > 16 || d->k > d->E) return MOK_ERR_SHAPE;
   if (d->H <= 0 || d->I <= 0 || d->H % 128 != 0 || d->I % 128 != 0) return MOK_ERR_SHAPE;
   if (d->T * (int64_t)d->k >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
@@ -28,6 +43,8 @@ mok_status check_desc(const mok_desc* d) {
   if ((int64_t)d->I * 2 * d->H >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
   if (d->tile_m != 0 && d->tile_m != 32 && d->tile_m != 64 && d->tile_m != 128) return MOK_ERR_SHAPE;
   if (d->grid < 0) return MOK_ERR_SHAPE;
+  // 32-bit offsets inside the token-axis operands of the MXFP8 weight gradients
+  if (is_mx(d) && mx_kmax(d) * std::max<int64_t>(d->H, 2LL * d->I) >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
   return MOK_OK;
 }
 
@@ -107,6 +124,64 @@ Layout layout_of(const mok_desc* d, int BM) {
   return L;
 }
 
+// MXFP8 buffer layout. Forward ring slot: quantised x rows, quantised h rows, partial
+// rows. Backward ring slot: quantised dY and dGU rows, partial rows, d-gate parts.
+// Then the stash of all micro-batches (array-major: micro-batch m's part of each
+// array at its m-th R rows) and the flush buffers.
+struct MxLayout {
+  size_t xq, xs, hq, hs, part, fslot, fwd;
+  size_t dyq, dys, dguq, dgus, bpart, dgp, bslot;
+  size_t st_counts, st_offsets, st_perm, st_dz, st_xs, st_dos, st_h, st_dgu;
+  size_t gcnt, pofs, rowmap, xt, xts, dot, dots, ht, hts, dgut, dguts, bwd;
+  int64_t kmax;
+};
+
+MxLayout mx_layout_of(const mok_desc* d) {
+  MxLayout L;
+  const int64_t T = d->T, R = d->T * d->k, H = d->H, I = d->I, E = d->E;
+  const int64_t M = mb_count_of(d), S = ring_of(d);
+  size_t o = 0;
+  L.xq = o; o = up(o + (size_t)(T * H));
+  L.xs = o; o = up(o + (size_t)(T * H / 32));
+  L.hq = o; o = up(o + (size_t)(R * I));
+  L.hs = o; o = up(o + (size_t)(R * I / 32));
+  L.part = o; o = up(o + (size_t)(2 * R * H));
+  L.fslot = o;
+  L.fwd = (size_t)S * L.fslot;
+  o = 0;
+  L.dyq = o; o = up(o + (size_t)(T * H));
+  L.dys = o; o = up(o + (size_t)(T * H / 32));
+  L.dguq = o; o = up(o + (size_t)(R * 2 * I));
+  L.dgus = o; o = up(o + (size_t)(R * 2 * I / 32));
+  L.bpart = o; o = up(o + (size_t)(2 * R * H));
+  L.dgp = o; o = up(o + (size_t)(4 * R * dh_ntiles(d->I)));
+  L.bslot = o;
+  o = (size_t)S * L.bslot;
+  L.st_counts = o; o = up(o + (size_t)(4 * M * E));
+  L.st_offsets = o; o = up(o + (size_t)(4 * M * (E + 1)));
+  L.st_perm = o; o = up(o + (size_t)(4 * M * R));
+  L.st_dz = o; o = up(o + (size_t)(4 * M * R));
+  L.st_xs = o; o = up(o + (size_t)(2 * M * R * H));
+  L.st_dos = o; o = up(o + (size_t)(2 * M * R * H));
+  L.st_h = o; o = up(o + (size_t)(2 * M * R * I));
+  L.st_dgu = o; o = up(o + (size_t)(2 * M * R * 2 * I));
+  L.kmax = mx_kmax(d);
+  const int64_t K = L.kmax;
+  L.gcnt = o; o = up(o + (size_t)(4 * E));
+  L.pofs = o; o = up(o + (size_t)(4 * (E + 1)));
+  L.rowmap = o; o = up(o + (size_t)(4 * K));
+  L.xt = o; o = up(o + (size_t)(H * K));
+  L.xts = o; o = up(o + (size_t)(H * K / 32));
+  L.dot = o; o = up(o + (size_t)(H * K));
+  L.dots = o; o = up(o + (size_t)(H * K / 32));
+  L.ht = o; o = up(o + (size_t)(I * K));
+  L.hts = o; o = up(o + (size_t)(I * K / 32));
+  L.dgut = o; o = up(o + (size_t)(2 * I * K));
+  L.dguts = o; o = up(o + (size_t)(2 * I * K / 32));
+  L.bwd = o;
+  return L;
+}
+
 mok_status resolve(const mok_desc* d, Layout* L, int* cus) {
   mok_status st = check_desc(d);
   if (st != MOK_OK) return st;
@@ -182,6 +257,89 @@ bool trace_on(const char* name) {
     }                                                                                               \
   } while (0)
 
+// MXFP8 backward of micro-batch d->mb_index (see mok_moe_backward in mok.h).
+mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int32_t* idx, const float* gate,
+                       const mok_weights* w, const void* wr, const void* saved, const void* dy, void* dx, void* dw1,
+                       void* dw2, float* dgate, void* dwr, void* ws) {
+  const bool flush = (d->flags & MOK_FLAG_WGRAD_DEFER) == 0;
+  if (flush) {
+    MOK_REQUIRE(dw1);
+    MOK_REQUIRE(dw2);
+    if (dwr != nullptr && !aligned16(dwr)) return MOK_ERR_ALIGN;
+  }
+  if (wr != nullptr && !aligned16(wr)) return MOK_ERR_ALIGN;
+  MOK_REQUIRE(ws);
+  const mok_mx_weights* q = w->mx;
+  if (c.R > 0) {
+    MOK_REQUIRE(x);
+    MOK_REQUIRE(idx);
+    MOK_REQUIRE(gate);
+    MOK_REQUIRE(saved);
+    MOK_REQUIRE(dy);
+    MOK_REQUIRE(dx);
+    MOK_REQUIRE(dgate);
+    if (q == nullptr) return MOK_ERR_NULL;
+    MOK_REQUIRE(q->w2tq);
+    MOK_REQUIRE(q->w2ts);
+    MOK_REQUIRE(q->w1tq);
+    MOK_REQUIRE(q->w1ts);
+  }
+  const Layout L = layout_of(d, c.BM);
+  const MxLayout X = mx_layout_of(d);
+  const char* sv = (const char*)saved;
+  char* wb = (char*)ws;
+  char* bs = wb + (size_t)(d->mb_index % ring_of(d)) * X.bslot;
+  const int64_t m = d->mb_index, R = c.R, H = c.H, I = c.I, E = c.E;
+  float* dz = (float*)(wb + X.st_dz) + m * R;
+  char* st_dgu = wb + X.st_dgu + (size_t)(m * R * 2 * I * 2);
+  if (c.R > 0) {
+    float* dgp = (float*)(bs + X.dgp);
+    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, dy, c.T, c.H, bs + X.dyq, bs + X.dys));
+    MOK_LAUNCH("dh", c.s, launch_dh_mx(c, bs + X.dyq, bs + X.dys, q->w2tq, q->w2ts, sv + L.au, sv + L.h, gate, st_dgu,
+                                       bs + X.dguq, bs + X.dgus, dgp));
+    MOK_LAUNCH("router_bwd", c.s, launch_router_bwd(c, dgp, gate, dgate, dz));
+    MOK_LAUNCH("dx", c.s, launch_dx_mx(c, bs + X.dguq, bs + X.dgus, q->w1tq, q->w1ts, bs + X.bpart));
+    MOK_LAUNCH("dx_reduce", c.s, launch_dx_reduce(c, bs + X.bpart, dz, idx, wr, dx));
+    // stash: routed-order x and dO = g*dy rows, h rows, perm
+    MOK_LAUNCH("quant", c.s, launch_gather_rows(c, x, nullptr, wb + X.st_xs + (size_t)(m * R * H * 2)));
+    MOK_LAUNCH("quant", c.s, launch_gather_rows(c, dy, gate, wb + X.st_dos + (size_t)(m * R * H * 2)));
+    MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_h + (size_t)(m * R * I * 2), sv + L.h, (size_t)(R * I * 2),
+                                            hipMemcpyDeviceToDevice, c.s));
+    MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_perm + (size_t)(m * R * 4), c.perm, (size_t)(R * 4),
+                                            hipMemcpyDeviceToDevice, c.s));
+  }
+  MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_counts + (size_t)(m * E * 4), c.counts, (size_t)(E * 4),
+                                          hipMemcpyDeviceToDevice, c.s));
+  MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_offsets + (size_t)(m * (E + 1) * 4), c.offsets,
+                                          (size_t)((E + 1) * 4), hipMemcpyDeviceToDevice, c.s));
+  if (!flush) return MOK_OK;
+
+  // weight gradients over the whole step
+  const int M = mb_count_of(d);
+  const int64_t K = X.kmax;
+  int32_t* gcnt = (int32_t*)(wb + X.gcnt);
+  int32_t* pofs = (int32_t*)(wb + X.pofs);
+  int32_t* rowmap = (int32_t*)(wb + X.rowmap);
+  MOK_LAUNCH("flush", c.s, launch_mx_flush_table(c, (const int32_t*)(wb + X.st_counts),
+                                                 (const int32_t*)(wb + X.st_offsets), M, gcnt, pofs, K, rowmap));
+  MOK_LAUNCH("flush", c.s, launch_mx_quant_cols(c, wb + X.st_dos, 0, H, rowmap, pofs + E, (int)K, (int)H, 1, K,
+                                                wb + X.dot, wb + X.dots));
+  MOK_LAUNCH("flush", c.s, launch_mx_quant_cols(c, wb + X.st_h, 0, I, rowmap, pofs + E, (int)K, (int)I, 1, K,
+                                                wb + X.ht, wb + X.hts));
+  MOK_LAUNCH("dw2", c.s, launch_dw_mx(c, pofs, wb + X.dot, wb + X.dots, wb + X.ht, wb + X.hts, dw2, (int)H, (int)I,
+                                      K));
+  MOK_LAUNCH("flush", c.s, launch_mx_quant_cols(c, wb + X.st_dgu, 0, 2 * I, rowmap, pofs + E, (int)K, (int)(2 * I), 1,
+                                                K, wb + X.dgut, wb + X.dguts));
+  MOK_LAUNCH("flush", c.s, launch_mx_quant_cols(c, wb + X.st_xs, 0, H, rowmap, pofs + E, (int)K, (int)H, 1, K,
+                                                wb + X.xt, wb + X.xts));
+  MOK_LAUNCH("dw1", c.s, launch_dw_mx(c, pofs, wb + X.dgut, wb + X.dguts, wb + X.xt, wb + X.xts, dw1, (int)(2 * I),
+                                      (int)H, K));
+  if (dwr != nullptr)
+    MOK_LAUNCH("dwr", c.s, launch_dwr_stash(c, (const float*)(wb + X.st_dz), (const int32_t*)(wb + X.st_perm),
+                                            wb + X.st_xs, gcnt, pofs, rowmap, dwr));
+  return MOK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +353,11 @@ mok_status mok_workspace_query(const mok_desc* d, mok_sizes* sizes) {
   sizes->saved = L.saved;
   sizes->fwd_ws = L.fwd;
   sizes->bwd_ws = L.bwd;
+  if (is_mx(d)) {
+    const MxLayout X = mx_layout_of(d);
+    sizes->fwd_ws = X.fwd;
+    sizes->bwd_ws = X.bwd;
+  }
   return MOK_OK;
 }
 
@@ -269,13 +432,29 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
   if (c.R == 0) return MOK_OK;
   MOK_REQUIRE(x);
   MOK_REQUIRE(gate);
-  MOK_REQUIRE(w->w1);
-  MOK_REQUIRE(w->w2);
   MOK_REQUIRE(y);
   MOK_REQUIRE(saved);
   MOK_REQUIRE(ws);
   const Layout L = layout_of(d, c.BM);
   char* sv = (char*)saved;
+  if (is_mx(d)) {
+    const mok_mx_weights* q = w->mx;
+    if (q == nullptr) return MOK_ERR_NULL;
+    MOK_REQUIRE(q->w1q);
+    MOK_REQUIRE(q->w1s);
+    MOK_REQUIRE(q->w2q);
+    MOK_REQUIRE(q->w2s);
+    const MxLayout X = mx_layout_of(d);
+    char* fs = (char*)ws + (size_t)(d->mb_index % ring_of(d)) * X.fslot;
+    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, x, c.T, c.H, fs + X.xq, fs + X.xs));
+    MOK_LAUNCH("fc1", c.s, launch_fc1_mx(c, fs + X.xq, fs + X.xs, q->w1q, q->w1s, sv + L.au, sv + L.h, fs + X.hq,
+                                         fs + X.hs));
+    MOK_LAUNCH("fc2", c.s, launch_fc2_mx(c, fs + X.hq, fs + X.hs, q->w2q, q->w2s, fs + X.part));
+    MOK_LAUNCH("combine", c.s, launch_combine(c, fs + X.part, gate, y));
+    return MOK_OK;
+  }
+  MOK_REQUIRE(w->w1);
+  MOK_REQUIRE(w->w2);
   MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, sv + L.au, sv + L.h));
   MOK_LAUNCH("fc2", c.s, launch_fc2(c, sv + L.h, w->w2, ws));
   MOK_LAUNCH("combine", c.s, launch_combine(c, ws, gate, y));
@@ -291,6 +470,7 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
   Ctx c;
   mok_status st = make_ctx(d, sched, stream, &c);
   if (st != MOK_OK) return st;
+  if (is_mx(d)) return mx_backward(d, c, x, idx, gate, w, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws);
   MOK_REQUIRE(dw1);
   MOK_REQUIRE(dw2);
   if (dwr != nullptr && !aligned16(dwr)) return MOK_ERR_ALIGN;
@@ -331,6 +511,37 @@ mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x,
   return MOK_OK;
 }
 
+mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w2, const mok_mx_weights* out,
+                                void* stream) {
+  mok_status st = check_desc(d);
+  if (st != MOK_OK) return st;
+  if (!is_mx(d)) return MOK_ERR_DTYPE;
+  if (out == nullptr) return MOK_ERR_NULL;
+  MOK_REQUIRE(w1);
+  MOK_REQUIRE(w2);
+  MOK_REQUIRE(out->w1q);
+  MOK_REQUIRE(out->w1s);
+  MOK_REQUIRE(out->w2q);
+  MOK_REQUIRE(out->w2s);
+  MOK_REQUIRE(out->w2tq);
+  MOK_REQUIRE(out->w2ts);
+  MOK_REQUIRE(out->w1tq);
+  MOK_REQUIRE(out->w1ts);
+  Ctx c{};
+  c.E = d->E;
+  c.H = d->H;
+  c.I = d->I;
+  c.s = (hipStream_t)stream;
+  const int64_t E = d->E, H = d->H, I = d->I;
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w1, E * 2 * I, (int)H, out->w1q, out->w1s));
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w2, E * H, (int)I, out->w2q, out->w2s));
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_cols(c, w2, H * I, I, nullptr, nullptr, (int)H, (int)I, (int)E, H,
+                                                out->w2tq, out->w2ts));
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_cols(c, w1, 2 * I * H, H, nullptr, nullptr, (int)(2 * I), (int)H, (int)E,
+                                                2 * I, out->w1tq, out->w1ts));
+  return MOK_OK;
+}
+
 mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity) {
   if (name == nullptr) {
     g_trace.events = nullptr;
@@ -362,6 +573,6 @@ const char* mok_status_string(mok_status s) {
   return "unknown status";
 }
 
-int32_t mok_version(void) { return 100; }
+int32_t mok_version(void) { return 200; }
 
 }  // extern "C"

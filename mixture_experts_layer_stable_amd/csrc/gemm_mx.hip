@@ -1,0 +1,445 @@
+// MXFP8 grouped expert GEMMs: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 x E4M3
+// operands, one E8M0 scale per 32 K-elements of every row of A and B, fp32
+// accumulation (expert GEMMs in MXFP8, dothoosh.com MoK page, "Technical details of
+// the MoK mechanism").
+//
+// Every operand is K-contiguous in HBM (the weights are pre-quantised in the
+// orientation each GEMM reads; the token-axis operands of the weight gradients are
+// quantised transposed), so one operand type serves all six GEMMs: the direct-to-
+// LDS K-contiguous tile of the bf16 core (OpK: 128-byte tile rows, here 128 E4M3
+// elements per K-tile) plus the rows' scale dwords (4 scale bytes = the 4 blocks of
+// the K-tile), DMA'd into the same ring stage.
+//
+// Operand lane layout of the 32x32x64 instruction (E4M3): lane l (half h = l/32)
+// holds row l%32, bytes 0..15 = k 16h..16h+15 and bytes 16..31 = k 32+16h..32+16h+15
+// of the 64-k step; the scale of row i for k-block q (k 32q..32q+31) comes from lane
+// i + 32q, byte `opsel` of its scale operand. In a 128-byte tile row the 64-k step ks
+// is chunks 4ks..4ks+3, so lane half h reads chunks 4ks+h and 4ks+2+h (OpK::frag
+// positions 2ks and 2ks+1) and scale byte 2ks+h of the row's dword (shifted down by
+// 8h, opsel 2ks).
+#include "gemm2.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace mok {
+
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMaxEx = 1024;
+constexpr int kMxStages = 3;
+
+// One-dword-per-lane DMA: lane l's 4 bytes land at LDS base + 4*l.
+__device__ __forceinline__ void dma4_sv(const char* sbase, uint32_t voff, char* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(l), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// Scale dwords of ROWS tile rows per K-tile. Wave w loads rows [w*RPW, (w+1)*RPW)
+// with lanes 0..RPW-1 (one DMA instruction per wave per stage, RPW >= 8 so the
+// instruction always has active lanes).
+template <int ROWS, int NF, int NW>
+struct OpScale {
+  static constexpr int RPW = ROWS / NW;
+  static_assert(ROWS % NW == 0 && RPW >= 8 && RPW <= 64, "scale rows per wave");
+  static constexpr int BYTES = ROWS * 4;
+  const char* sbase;
+  uint32_t voff;
+  uint32_t foff[NF];
+  bool active;
+
+  // rowoff(row) -> byte offset of the row's first scale byte from sbase_ (< 2 GiB)
+  template <class F, class G>
+  __device__ __forceinline__ void init(const void* sbase_, F rowoff, G frow, int wave, int lane) {
+    sbase = reinterpret_cast<const char*>(sbase_);
+    active = lane < RPW;
+    voff = rowoff(wave * RPW + (active ? lane : 0));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) foff[f] = 4u * (uint32_t)(frow(f) + (lane & 31));
+  }
+  __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
+    const char* b = uniform_ptr(sbase + (int64_t)kt * 4);
+    if (active) dma4_sv(b, voff, stage + wave * RPW * 4);
+  }
+  __device__ __forceinline__ uint32_t get(const char* stage, int f, int lane) const {
+    return *reinterpret_cast<const uint32_t*>(stage + foff[f]) >> (8 * (lane >> 5));
+  }
+};
+
+__device__ __forceinline__ v8i32_t join8(const uint4& lo, const uint4& hi) {
+  v8i32_t v;
+  v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
+  v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
+  return v;
+}
+
+// One 64-k step of the K-tile in `cur` (opsel = byte 2*KS of the shifted scale dwords).
+template <int KS, class Tl, class OA, class OB>
+__device__ __forceinline__ void mx_kstep(const OA& oa, const OB& ob, const char* ca, const char* cb,
+                                         const uint32_t (&xa)[Tl::FM], const uint32_t (&xb)[Tl::FN],
+                                         f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  v8i32_t a[Tl::FM], b[Tl::FN];
+#pragma unroll
+  for (int fm = 0; fm < Tl::FM; ++fm) a[fm] = join8(oa.frag(ca, fm, 2 * KS), oa.frag(ca, fm, 2 * KS + 1));
+#pragma unroll
+  for (int fn = 0; fn < Tl::FN; ++fn) b[fn] = join8(ob.frag(cb, fn, 2 * KS), ob.frag(cb, fn, 2 * KS + 1));
+#pragma unroll
+  for (int fm = 0; fm < Tl::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fm], b[fn], acc[fm][fn], 0, 0, 2 * KS,
+                                                                    (int)xa[fm], 2 * KS, (int)xb[fn]);
+}
+
+// STAGES-deep ring as in the bf16 core; a stage holds A rows, B rows, A scales, B scales.
+template <class Tl, int STAGES, class OA, class OB, class SA, class SB>
+__device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
+                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  constexpr int OFF_B = OA::BYTES, OFF_SA = OA::BYTES + OB::BYTES, OFF_SB = OFF_SA + SA::BYTES;
+  constexpr int STG = OFF_SB + SB::BYTES;
+  constexpr int NI = OA::NI + OB::NI + 2;
+  zero_acc<Tl>(acc);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < KT) {
+      char* st = smem + s * STG;
+      oa.issue(s, st, wave);
+      ob.issue(s, st + OFF_B, wave);
+      sa.issue(s, st + OFF_SA, wave);
+      sb.issue(s, st + OFF_SB, wave);
+    }
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const int ahead = KT - 1 - kt;
+    wait_tiles_behind<STAGES, NI>(ahead < STAGES - 2 ? ahead : STAGES - 2);
+    ring_barrier();
+    const int nk = kt + STAGES - 1;
+    if (nk < KT) {
+      char* st = smem + (nk % STAGES) * STG;
+      oa.issue(nk, st, wave);
+      ob.issue(nk, st + OFF_B, wave);
+      sa.issue(nk, st + OFF_SA, wave);
+      sb.issue(nk, st + OFF_SB, wave);
+    }
+    const char* cur = smem + (kt % STAGES) * STG;
+    uint32_t xa[Tl::FM], xb[Tl::FN];
+#pragma unroll
+    for (int fm = 0; fm < Tl::FM; ++fm) xa[fm] = sa.get(cur + OFF_SA, fm, lane);
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; ++fn) xb[fn] = sb.get(cur + OFF_SB, fn, lane);
+    mx_kstep<0, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    mx_kstep<1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+  }
+  __syncthreads();
+}
+
+template <int BM, int BN>
+using RowTilingMx = Tiling<BM, BN, (BM == 32 ? 1 : 2), 4>;
+
+struct MxRowArgs {
+  Sched sc;
+  const uint8_t* aq;  // fc1: x; fc2: h; dh: dy; dx: dgu  (E4M3 rows)
+  const uint8_t* as;  // their scales
+  const uint8_t* wq;  // fc1: w1q; fc2: w2q; dh: w2tq; dx: w1tq
+  const uint8_t* ws;
+  bf16* out0;         // fc1: au; fc2/dx: part; dh: dgu (bf16)
+  bf16* out1;         // fc1: h
+  uint8_t* oq;        // fc1: h quantised along I; dh: dgu quantised along 2I
+  uint8_t* os;
+  const bf16* au;     // dh
+  const bf16* h;      // dh
+  const float* gate;  // dh
+  float* dgp;         // dh
+  int H, I, k, R;
+};
+
+enum MxKind { MFC1 = 0, MFC2 = 1, MDH = 2, MDX = 3 };
+
+template <int KIND, class Tl>
+__global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
+  using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
+  using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  constexpr int STG = OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES;
+  __shared__ __align__(1024) char smem[kMxStages * STG];
+  __shared__ int s_ts[kMaxEx + 1];
+  __shared__ int s_slot[Tl::BM];
+  __shared__ float s_red[KIND == MDH ? Tl::BN / 32 : 1][KIND == MDH ? Tl::BM : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  const int I2 = 2 * a.I;
+  const int N = KIND == MFC1 ? I2 : (KIND == MFC2 || KIND == MDX ? a.H : a.I);
+  const int K = KIND == MFC1 || KIND == MDH ? a.H : (KIND == MFC2 ? a.I : I2);
+  const int KB = K / 32;  // scale bytes per row
+  load_tile_start(a.sc, s_ts);
+  for_each_row_tile(a.sc, s_ts, N / Tl::BN, [&](const RowTile& t) {
+    __syncthreads();
+    for (int i = tid; i < Tl::BM; i += Tl::NT) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
+    __syncthreads();
+    const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
+    const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
+    OA oa;
+    SA sa;
+    if constexpr (KIND == MFC1 || KIND == MDH) {
+      // pull dispatch / reverse-combine: token rows gathered through perm (padding rows re-read row 0)
+      const auto tok = [&](int row) { return (uint32_t)(s_slot[row < t.nrows ? row : 0] / a.k); };
+      oa.init(a.aq, [&](int row) -> uint32_t { return tok(row) * (uint32_t)K; }, frow_a, wave, lane);
+      sa.init(a.as, [&](int row) -> uint32_t { return tok(row) * (uint32_t)KB; }, frow_a, wave, lane);
+    } else {
+      const auto rr = [&](int row) { return (uint32_t)(row < t.nrows ? row : 0); };
+      oa.init(a.aq + (int64_t)t.row0 * K, [&](int row) -> uint32_t { return rr(row) * (uint32_t)K; }, frow_a, wave,
+              lane);
+      sa.init(a.as + (int64_t)t.row0 * KB, [&](int row) -> uint32_t { return rr(row) * (uint32_t)KB; }, frow_a,
+              wave, lane);
+    }
+    OB ob;
+    SB sb;
+    if constexpr (KIND == MFC1) {
+      // W1 rows with gate/up interleaved per 32-column block of the tile
+      const int cbase = t.n * (Tl::BN / 2);
+      const auto wrow = [&](int j) -> uint32_t {
+        const int wj = j / Tl::WTN, fn = (j % Tl::WTN) >> 5;
+        const int c = cbase + wj * (Tl::WTN / 2) + (fn >> 1) * 32 + (j & 31);
+        return (uint32_t)((fn & 1) ? a.I + c : c);
+      };
+      ob.init(a.wq + (int64_t)t.e * I2 * a.H, [&](int j) -> uint32_t { return wrow(j) * (uint32_t)K; }, frow_b, wave,
+              lane);
+      sb.init(a.ws + (int64_t)t.e * I2 * KB, [&](int j) -> uint32_t { return wrow(j) * (uint32_t)KB; }, frow_b, wave,
+              lane);
+    } else {
+      // weight rows n*BN + j of expert e's [N][K] matrix
+      const int64_t r0 = (int64_t)t.e * N + (int64_t)t.n * Tl::BN;
+      ob.init(a.wq + r0 * K, [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)K; }, frow_b, wave, lane);
+      sb.init(a.ws + r0 * KB, [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)KB; }, frow_b, wave, lane);
+    }
+    f32x16_t acc[Tl::FM][Tl::FN];
+    main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, K / 128, smem, wave, lane, acc);
+
+    if constexpr (KIND == MFC1) {
+      const int cbase = t.n * (Tl::BN / 2);
+      epilogue16<Tl, true>(acc, smem, wave, wm, wn, lane,
+                           [&](int row, int col, const float (&g)[16], const float (&u)[16]) {
+        if (row >= t.nrows) return;  // both lanes of a pair share the row
+        const int64_t R = t.row0 + row;
+        const int wj = col / Tl::WTN, cw = col % Tl::WTN;
+        const int c = cbase + wj * (Tl::WTN / 2) + (cw >> 6) * 32 + (cw & 31);
+        float hv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+        round16_bf16(hv);
+        store16<bf16>(a.out0 + R * I2 + c, g);
+        store16<bf16>(a.out0 + R * I2 + a.I + c, u);
+        store16<bf16>(a.out1 + R * a.I + c, hv);
+        uint32_t sbyte;
+        const uint4 q = mx_quant16_pair(hv, &sbyte);
+        stg16(a.oq + R * a.I + c, q);
+        if ((lane & 1) == 0) a.os[R * (a.I / 32) + (c >> 5)] = (uint8_t)sbyte;
+      });
+    } else if constexpr (KIND == MFC2 || KIND == MDX) {
+      epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane,
+                            [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+        if (row < t.nrows) store16<bf16>(a.out0 + (int64_t)s_slot[row] * a.H + t.n * Tl::BN + col, g);
+      });
+    } else {  // MDH
+      epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane,
+                            [&](int row, int col, const float (&dA)[16], const float (&)[16]) {
+        float part = 0.0f;
+        if (row < t.nrows) {  // both lanes of a pair share the row
+          const int64_t R = t.row0 + row;
+          const int c = t.n * Tl::BN + col;
+          const float g = a.gate[s_slot[row]];
+          float av[16], uv[16], hv[16], da[16], du[16];
+          load16<bf16>(a.au + R * I2 + c, av);
+          load16<bf16>(a.au + R * I2 + a.I + c, uv);
+          load16<bf16>(a.h + R * a.I + c, hv);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            part = __builtin_fmaf(dA[i], hv[i], part);
+            const float dh = g * dA[i];
+            const float sg = 1.0f / (1.0f + expf(-av[i]));
+            da[i] = dh * uv[i] * sg * (1.0f + av[i] * (1.0f - sg));
+            du[i] = dh * av[i] * sg;
+          }
+          round16_bf16(da);
+          round16_bf16(du);
+          store16<bf16>(a.out0 + R * I2 + c, da);
+          store16<bf16>(a.out0 + R * I2 + a.I + c, du);
+          uint32_t s1, s2;
+          const uint4 q1 = mx_quant16_pair(da, &s1);
+          const uint4 q2 = mx_quant16_pair(du, &s2);
+          stg16(a.oq + R * I2 + c, q1);
+          stg16(a.oq + R * I2 + a.I + c, q2);
+          if ((lane & 1) == 0) {
+            a.os[R * (I2 / 32) + (c >> 5)] = (uint8_t)s1;
+            a.os[R * (I2 / 32) + ((a.I + c) >> 5)] = (uint8_t)s2;
+          }
+        }
+        const float other = __shfl_xor(part, 1);
+        const float blk = (lane & 1) ? other + part : part + other;
+        if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+      });
+      for (int i = tid; i < t.nrows; i += Tl::NT) {
+        float s = 0.0f;
+#pragma unroll
+        for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
+        a.dgp[(int64_t)t.n * a.R + t.row0 + i] = s;
+      }
+    }
+  });
+}
+
+// Weight gradients: out[e] [M][N] = sum over k in e's padded segment of A[m][k] B[n][k],
+// A [M][kld] and B [N][kld] E4M3 with scales [M][kld/32], [N][kld/32]; e's segment is
+// columns pofs[e] .. pofs[e+1] (a multiple of 128; empty -> zeros written).
+struct MxDwArgs {
+  const int32_t* pofs;
+  const uint8_t *aq, *as, *bq, *bs;
+  void* out;
+  int M, N;
+  int64_t kld;
+};
+
+template <class Tl, typename TO>
+__global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
+  using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
+  using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  __shared__ __align__(1024) char smem[kMxStages * (OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  const int e = L / (MT * NT);
+  const int rem = L - e * MT * NT;
+  const int mt = rem / NT, nt = rem - mt * NT;
+  const int64_t k0 = a.pofs[e];
+  const int KT = (int)((a.pofs[e + 1] - k0) / 128);
+  const int64_t kb = a.kld / 32;
+  const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
+  const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
+  OA oa;
+  SA sa;
+  OB ob;
+  SB sb;
+  oa.init(a.aq + (int64_t)mt * Tl::BM * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+          frow_a, wave, lane);
+  sa.init(a.as + (int64_t)mt * Tl::BM * kb + k0 / 32, [&](int r) -> uint32_t { return (uint32_t)(r * kb); }, frow_a,
+          wave, lane);
+  ob.init(a.bq + (int64_t)nt * Tl::BN * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+          frow_b, wave, lane);
+  sb.init(a.bs + (int64_t)nt * Tl::BN * kb + k0 / 32, [&](int r) -> uint32_t { return (uint32_t)(r * kb); }, frow_b,
+          wave, lane);
+  f32x16_t acc[Tl::FM][Tl::FN];
+  main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+  TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
+  epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
+    store16<TO>(out + (int64_t)row * a.N + col, g);
+  });
+}
+
+// ---------------------------------------------------------------------------
+static Sched sched_of_mx(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+
+template <int KIND, int BM, int BN>
+static hipError_t row_launch_mx(const Ctx& c, const MxRowArgs& a, int N) {
+  using Tl = RowTilingMx<BM, BN>;
+  int g = c.grid > 0 ? c.grid : c.num_cu;
+  const int64_t upper = (int64_t)c.max_tiles * (N / BN);
+  if (g > upper) g = (int)std::max<int64_t>(upper, 1);
+  hipLaunchKernelGGL((row_gemm_mx_kernel<KIND, Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a);
+  return hipGetLastError();
+}
+
+template <int KIND, int BN>
+static hipError_t row_bm_mx(const Ctx& c, const MxRowArgs& a, int N) {
+  switch (c.BM) {
+    case 32: return row_launch_mx<KIND, 32, BN>(c, a, N);
+    case 64: return row_launch_mx<KIND, 64, BN>(c, a, N);
+    case 128: return row_launch_mx<KIND, 128, BN>(c, a, N);
+  }
+  return hipErrorInvalidValue;
+}
+
+static MxRowArgs mx_args(const Ctx& c) {
+  MxRowArgs a{};
+  a.sc = sched_of_mx(c);
+  a.H = c.H;
+  a.I = c.I;
+  a.k = c.k;
+  a.R = c.R;
+  return a;
+}
+
+hipError_t launch_fc1_mx(const Ctx& c, const void* xq, const void* xs, const void* w1q, const void* w1s, void* au,
+                         void* h, void* hq, void* hs) {
+  MxRowArgs a = mx_args(c);
+  a.aq = (const uint8_t*)xq;
+  a.as = (const uint8_t*)xs;
+  a.wq = (const uint8_t*)w1q;
+  a.ws = (const uint8_t*)w1s;
+  a.out0 = (bf16*)au;
+  a.out1 = (bf16*)h;
+  a.oq = (uint8_t*)hq;
+  a.os = (uint8_t*)hs;
+  return row_bm_mx<MFC1, 256>(c, a, 2 * c.I);
+}
+
+hipError_t launch_fc2_mx(const Ctx& c, const void* hq, const void* hs, const void* w2q, const void* w2s, void* part) {
+  MxRowArgs a = mx_args(c);
+  a.aq = (const uint8_t*)hq;
+  a.as = (const uint8_t*)hs;
+  a.wq = (const uint8_t*)w2q;
+  a.ws = (const uint8_t*)w2s;
+  a.out0 = (bf16*)part;
+  return bn_rows(c.H) == 256 ? row_bm_mx<MFC2, 256>(c, a, c.H) : row_bm_mx<MFC2, 128>(c, a, c.H);
+}
+
+hipError_t launch_dh_mx(const Ctx& c, const void* dyq, const void* dys, const void* w2tq, const void* w2ts,
+                        const void* au, const void* h, const float* gate, void* dgu, void* dguq, void* dgus,
+                        float* dgp) {
+  MxRowArgs a = mx_args(c);
+  a.aq = (const uint8_t*)dyq;
+  a.as = (const uint8_t*)dys;
+  a.wq = (const uint8_t*)w2tq;
+  a.ws = (const uint8_t*)w2ts;
+  a.out0 = (bf16*)dgu;
+  a.oq = (uint8_t*)dguq;
+  a.os = (uint8_t*)dgus;
+  a.au = (const bf16*)au;
+  a.h = (const bf16*)h;
+  a.gate = gate;
+  a.dgp = dgp;
+  return bn_rows(c.I) == 256 ? row_bm_mx<MDH, 256>(c, a, c.I) : row_bm_mx<MDH, 128>(c, a, c.I);
+}
+
+hipError_t launch_dx_mx(const Ctx& c, const void* dguq, const void* dgus, const void* w1tq, const void* w1ts,
+                        void* part) {
+  MxRowArgs a = mx_args(c);
+  a.aq = (const uint8_t*)dguq;
+  a.as = (const uint8_t*)dgus;
+  a.wq = (const uint8_t*)w1tq;
+  a.ws = (const uint8_t*)w1ts;
+  a.out0 = (bf16*)part;
+  return bn_rows(c.H) == 256 ? row_bm_mx<MDX, 256>(c, a, c.H) : row_bm_mx<MDX, 128>(c, a, c.H);
+}
+
+template <class Tl>
+static hipError_t dw_launch_mx(const Ctx& c, const MxDwArgs& a) {
+  const int64_t blocks = (int64_t)c.E * (a.M / Tl::BM) * (a.N / Tl::BN);
+  if (blocks == 0) return hipSuccess;
+  if (c.wgrad_f32)
+    hipLaunchKernelGGL((dw_mx_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
+  else
+    hipLaunchKernelGGL((dw_mx_kernel<Tl, bf16>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const void* as, const void* bq,
+                        const void* bs, void* out, int M, int N, int64_t kld) {
+  MxDwArgs a{pofs, (const uint8_t*)aq, (const uint8_t*)as, (const uint8_t*)bq, (const uint8_t*)bs, out, M, N, kld};
+  if (N % 256 == 0) return dw_launch_mx<Tiling<128, 256, 2, 4>>(c, a);
+  return dw_launch_mx<Tiling<128, 128, 2, 2>>(c, a);
+}
+
+}  // namespace mok

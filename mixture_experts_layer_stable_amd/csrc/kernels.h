@@ -55,6 +55,31 @@ hipError_t launch_dw1_bf16(const Ctx& c, const void* dgu, const void* xs, void* 
 // dst[r] = src[perm[r] / k] (times gate[perm[r]] when gate != nullptr), bf16 rows of H
 hipError_t launch_gather_rows(const Ctx& c, const void* src, const float* gate, void* dst);
 
+// MXFP8: quantisers (E4M3 elements + E8M0 scale bytes per 32 along K)
+// rows x F bf16 -> q [rows][F], s [rows][F/32] (blocks along each row)
+hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s);
+// transposed, blocks along rows: q [mats][F][out_ld], s [mats][F][out_ld/32]; logical
+// row r of matrix z reads physical row rowmap[r] (or r) of src + z*src_mat (ld elements
+// per row); K logical rows (multiple of 128), row blocks at or past *kdev skipped
+hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, int64_t ld, const int32_t* rowmap,
+                                const int32_t* kdev, int K, int F, int mats, int64_t out_ld, void* q, void* s);
+// per-expert rows over M stashed micro-batches, 128-padded segment offsets, row map
+hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int32_t* offsets, int M, int32_t* gcnt,
+                                 int32_t* pofs, int64_t kmax, int32_t* rowmap);
+hipError_t launch_dwr_stash(const Ctx& c, const float* dz, const int32_t* perm, const void* xs, const int32_t* gcnt,
+                            const int32_t* pofs, const int32_t* rowmap, void* dwr);
+// MXFP8 grouped GEMMs
+hipError_t launch_fc1_mx(const Ctx& c, const void* xq, const void* xs, const void* w1q, const void* w1s, void* au,
+                         void* h, void* hq, void* hs);
+hipError_t launch_fc2_mx(const Ctx& c, const void* hq, const void* hs, const void* w2q, const void* w2s, void* part);
+hipError_t launch_dh_mx(const Ctx& c, const void* dyq, const void* dys, const void* w2tq, const void* w2ts,
+                        const void* au, const void* h, const float* gate, void* dgu, void* dguq, void* dgus,
+                        float* dgp);
+hipError_t launch_dx_mx(const Ctx& c, const void* dguq, const void* dgus, const void* w1tq, const void* w1ts,
+                        void* part);
+hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const void* as, const void* bq,
+                        const void* bs, void* out, int M, int N, int64_t kld);
+
 // Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
 inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }
 inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }

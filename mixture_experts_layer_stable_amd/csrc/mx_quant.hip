@@ -1,0 +1,218 @@
+// MXFP8 quantisers and the deferred weight-gradient bookkeeping (HBM-bound kernels).
+//
+//  quant_rows   blocks of 32 along each row: x and dY rows (K = H of fc1 / dh) and the
+//               forward weight orientations W1 (rows along H) and W2 (rows along I).
+//  quant_cols   blocks of 32 along the row axis, written transposed (feature-major,
+//               K = rows contiguous): W2^T and W1^T for dh / dx, and the token-axis
+//               operands of the weight-gradient GEMMs (dO, h, dGU, x over each
+//               expert's routed rows of the whole step).
+//  flush_table  per expert: rows over all stashed micro-batches, and the K offset of its
+//               segment in the token-axis operands (segments padded to 128 rows with
+//               zero rows, i.e. all-zero blocks, which add nothing).
+//  rowmap       padded segment row -> stash row (micro-batch m's routed row r is stash
+//               row m*R + r); -1 for padding.
+//  dwr_stash    dWr[e] = sum over e's rows of the step, in micro-batch then slot order,
+//               of dz_s * x_t (fp32 fused multiply-adds in that order).
+#include "gemm.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace mok {
+
+static unsigned nblk(int64_t n, int b = 256) { return (unsigned)((n + b - 1) / b); }
+
+// nvec = (rows * F) / 16 sixteen-element vectors; F % 32 == 0, so vector pairs
+// (2j, 2j+1) are exactly the 32-element blocks and block b's scale is s[b].
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restrict__ src, int64_t nvec,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= nvec) return;  // nvec and blockDim are even: a pair leaves together
+  float f[16];
+  load16<bf16>(src + v * 16, f);
+  uint32_t sb;
+  const uint4 o = mx_quant16_pair(f, &sb);
+  stg16(q + v * 16, o);
+  if ((v & 1) == 0) s[v >> 1] = (uint8_t)sb;
+}
+
+hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s) {
+  const int64_t nvec = rows * (F / 16);
+  if (nvec == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(nblk(nvec)), dim3(256), 0, c.s, (const bf16*)src, nvec, (uint8_t*)q,
+                     (uint8_t*)s);
+  return hipGetLastError();
+}
+
+// Transposing quantiser. Matrix z = blockIdx.z; logical row r in [0, K) reads
+// physical row rowmap[r] (rowmap != nullptr; < 0 = zero row) or r of
+// src + z * src_mat, ld elements per physical row; feature f in [0, F).
+// Writes q[(z*F + f) * out_ld + r] and s[(z*F + f) * (out_ld/32) + r/32].
+// Workgroup: 128 logical rows x 64 features; wave w quantises block w (32 rows)
+// of the 64 features. Row blocks at or past *kdev (when given) are skipped.
+struct ColQuantArgs {
+  const bf16* src;
+  int64_t src_mat, ld;
+  const int32_t* rowmap;
+  const int32_t* kdev;
+  int F;
+  int64_t out_ld;
+  uint8_t* q;
+  uint8_t* s;
+};
+
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
+  __shared__ float tile[128][65];
+  const int r0 = blockIdx.x * 128, f0 = blockIdx.y * 64, z = blockIdx.z;
+  if (a.kdev != nullptr && r0 >= *a.kdev) return;
+  const bf16* src = a.src + (int64_t)z * a.src_mat;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = threadIdx.x + 256 * i;  // 128 rows x 8 vectors of 8 features
+    const int row = v >> 3, c8 = (v & 7) * 8;
+    const int r = r0 + row;
+    const int64_t p = a.rowmap != nullptr ? (int64_t)a.rowmap[r] : (int64_t)r;
+    float f[8];
+    if (p >= 0) {
+      unpack(ldg16(src + p * a.ld + f0 + c8), f, (bf16*)nullptr);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tile[row][c8 + q] = f[q];
+  }
+  __syncthreads();
+  const int f = threadIdx.x & 63, b = threadIdx.x >> 6;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][f]));
+  const uint32_t sb = mx_scale_byte(m);
+  const float inv = mx_inv_scale(sb);
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = 32 * b + 4 * j;
+    w[j] = mx_pack4(tile[i][f], tile[i + 1][f], tile[i + 2][f], tile[i + 3][f], inv);
+  }
+  const int64_t orow = (int64_t)z * a.F + f0 + f;
+  uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;
+  stg16(qo, make_uint4(w[0], w[1], w[2], w[3]));
+  stg16(qo + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  a.s[orow * (a.out_ld / 32) + r0 / 32 + b] = (uint8_t)sb;
+}
+
+hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, int64_t ld, const int32_t* rowmap,
+                                const int32_t* kdev, int K, int F, int mats, int64_t out_ld, void* q, void* s) {
+  if (K == 0 || F == 0 || mats == 0) return hipSuccess;
+  ColQuantArgs a{(const bf16*)src, src_mat, ld, rowmap, kdev, F, out_ld, (uint8_t*)q, (uint8_t*)s};
+  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3(K / 128, F / 64, mats), dim3(256), 0, c.s, a);
+  return hipGetLastError();
+}
+
+// One workgroup of 1024 threads (E <= 1024). counts is [M][E].
+__global__ __launch_bounds__(1024) void mx_flush_table_kernel(const int32_t* __restrict__ counts, int M, int E,
+                                                              int32_t* __restrict__ gcnt, int32_t* __restrict__ pofs) {
+  __shared__ int sc[1024];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E)
+    for (int m = 0; m < M; ++m) c += counts[(int64_t)m * E + e];
+  const int p = (c + 127) & ~127;
+  sc[e] = p;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
+    const int v = e >= d ? sc[e - d] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    gcnt[e] = c;
+    pofs[e] = sc[e] - p;
+  }
+  if (e == E - 1) pofs[E] = sc[e];
+}
+
+// offsets is [M][E+1]; one thread per padded row p < kmax.
+__global__ __launch_bounds__(256) void mx_rowmap_kernel(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets, int M, int E, int R,
+                                                        const int32_t* __restrict__ gcnt,
+                                                        const int32_t* __restrict__ pofs, int64_t kmax,
+                                                        int32_t* __restrict__ rowmap) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= kmax || p >= pofs[E]) return;
+  int lo = 0, hi = E;  // pofs[lo] <= p < pofs[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pofs[mid] <= p) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  int j = (int)(p - pofs[e]);
+  int out = -1;
+  if (j < gcnt[e]) {
+    for (int m = 0; m < M; ++m) {
+      const int cm = counts[(int64_t)m * E + e];
+      if (j < cm) {
+        out = m * R + offsets[(int64_t)m * (E + 1) + e] + j;
+        break;
+      }
+      j -= cm;
+    }
+  }
+  rowmap[p] = out;
+}
+
+hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int32_t* offsets, int M, int32_t* gcnt,
+                                 int32_t* pofs, int64_t kmax, int32_t* rowmap) {
+  hipLaunchKernelGGL(mx_flush_table_kernel, dim3(1), dim3(1024), 0, c.s, counts, M, c.E, gcnt, pofs);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(mx_rowmap_kernel, dim3(nblk(kmax)), dim3(256), 0, c.s, counts, offsets, M, c.E, c.R, gcnt, pofs,
+                     kmax, rowmap);
+  return hipGetLastError();
+}
+
+// dz and perm are [M][R] (micro-batch m's slot-indexed dz and its schedule perm);
+// xs is [M*R][H] (micro-batch m's x rows in routed order at rows m*R ..).
+template <typename TO>
+__global__ __launch_bounds__(256) void dwr_stash_kernel(const float* __restrict__ dz, const int32_t* __restrict__ perm,
+                                                        const bf16* __restrict__ xs, const int32_t* __restrict__ gcnt,
+                                                        const int32_t* __restrict__ pofs,
+                                                        const int32_t* __restrict__ rowmap, TO* __restrict__ dwr,
+                                                        int E, int H, int R) {
+  const int vpr = H / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)E * vpr) return;
+  const int e = (int)(gid / vpr);
+  const int h0 = (int)(gid - (int64_t)e * vpr) * 8;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  const int n = gcnt[e];
+  const int32_t* rm = rowmap + pofs[e];
+  for (int j = 0; j < n; ++j) {
+    const int row = rm[j];
+    const int m = row / R;
+    const float d = dz[(int64_t)m * R + perm[row]];
+    float f[8];
+    unpack(ldg16(xs + (int64_t)row * H + h0), f, (bf16*)nullptr);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+  }
+  TO* o = dwr + (int64_t)e * H + h0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) Elem<TO>::put(o, q, acc[q]);
+}
+
+hipError_t launch_dwr_stash(const Ctx& c, const float* dz, const int32_t* perm, const void* xs, const int32_t* gcnt,
+                            const int32_t* pofs, const int32_t* rowmap, void* dwr) {
+  const int64_t n = (int64_t)c.E * (c.H / 8);
+  if (c.wgrad_f32)
+    hipLaunchKernelGGL((dwr_stash_kernel<float>), dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt,
+                       pofs, rowmap, (float*)dwr, c.E, c.H, c.R);
+  else
+    hipLaunchKernelGGL((dwr_stash_kernel<bf16>), dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt,
+                       pofs, rowmap, (bf16*)dwr, c.E, c.H, c.R);
+  return hipGetLastError();
+}
+
+}  // namespace mok

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmok.so")
 
 F32, BF16, MXFP8 = 0, 1, 2
 FLAG_WGRAD_F32 = 1
+FLAG_WGRAD_DEFER = 2
 DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8}
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -35,11 +36,19 @@ class MokError(RuntimeError):
 class _Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("act", ctypes.c_int32), ("gemm", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("tile_m", ctypes.c_int32), ("grid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("tile_m", ctypes.c_int32), ("grid", ctypes.c_int32), ("mb_index", ctypes.c_int32),
+                ("mb_count", ctypes.c_int32), ("ring", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+MX_FIELDS = ("w1q", "w1s", "w2q", "w2s", "w2tq", "w2ts", "w1tq", "w1ts")
+
+
+class _MxWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in MX_FIELDS]
 
 
 class _Weights(ctypes.Structure):
-    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("mx", ctypes.POINTER(_MxWeights))]
 
 
 class _Sizes(ctypes.Structure):
@@ -72,6 +81,7 @@ def _load():
         "mok_schedule_build": [D, P, P, P],
         "mok_moe_forward": [D, P, P, P, ctypes.POINTER(_Weights), P, P, P, P],
         "mok_moe_backward": [D, P, P, P, P, ctypes.POINTER(_Weights), P, P, P, P, P, P, P, P, P, P],
+        "mok_weights_quantize": [D, P, P, ctypes.POINTER(_MxWeights), P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -92,8 +102,8 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_route",
-           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_status_string", "mok_version",
-           "mok_trace_set", "mok_trace_count", "mok_trace_name")
+           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_weights_quantize", "mok_status_string",
+           "mok_version", "mok_trace_set", "mok_trace_count", "mok_trace_name")
 
 
 @dataclass
@@ -108,10 +118,18 @@ class Desc:
     flags: int = 0
     tile_m: int = 0
     grid: int = 0
+    mb_index: int = 0
+    mb_count: int = 1
+    ring: int = 1
 
     def c(self) -> _Desc:
         g = self.act if self.gemm is None else self.gemm
-        return _Desc(self.T, self.H, self.E, self.k, self.I, self.act, g, self.flags, self.tile_m, self.grid, 0)
+        return _Desc(self.T, self.H, self.E, self.k, self.I, self.act, g, self.flags, self.tile_m, self.grid,
+                     self.mb_index, self.mb_count, self.ring, 0)
+
+    @property
+    def mx(self) -> bool:
+        return self.gemm == MXFP8
 
     @property
     def R(self) -> int:
@@ -167,14 +185,43 @@ def schedule_build(d: Desc, idx, sched, stream=None):
     _check(_lib.mok_schedule_build(ctypes.byref(d.c()), _p(idx), _p(sched), _stream(stream)), "mok_schedule_build")
 
 
-def moe_forward(d: Desc, sched, x, gate, w1, w2, y, saved, ws, stream=None):
-    w = _Weights(w1.data_ptr(), w2.data_ptr())
+class MxWeights:
+    """Device tensors of the MXFP8 weight orientations (mok_mx_weights), filled by weights_quantize."""
+
+    def __init__(self, d: Desc, device="cuda"):
+        E, H, I = d.E, d.H, d.I
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.w1q, self.w1s = torch.empty(E, 2 * I, H, **u8), torch.empty(E, 2 * I, H // 32, **u8)
+        self.w2q, self.w2s = torch.empty(E, H, I, **u8), torch.empty(E, H, I // 32, **u8)
+        self.w2tq, self.w2ts = torch.empty(E, I, H, **u8), torch.empty(E, I, H // 32, **u8)
+        self.w1tq, self.w1ts = torch.empty(E, H, 2 * I, **u8), torch.empty(E, H, 2 * I // 32, **u8)
+
+    def c(self) -> _MxWeights:
+        return _MxWeights(*[getattr(self, n).data_ptr() for n in MX_FIELDS])
+
+
+def weights_quantize(d: Desc, w1, w2, mxw: MxWeights, stream=None):
+    q = mxw.c()
+    _check(_lib.mok_weights_quantize(ctypes.byref(d.c()), _p(w1), _p(w2), ctypes.byref(q), _stream(stream)),
+           "mok_weights_quantize")
+
+
+def _weights(w1, w2, mxw):
+    q = None if mxw is None else mxw.c()
+    w = _Weights(None if w1 is None else w1.data_ptr(), None if w2 is None else w2.data_ptr(),
+                 None if q is None else ctypes.pointer(q))
+    return w, q     # q must outlive the call
+
+
+def moe_forward(d: Desc, sched, x, gate, w1, w2, y, saved, ws, stream=None, mxw: Optional[MxWeights] = None):
+    w, _keep = _weights(w1, w2, mxw)
     _check(_lib.mok_moe_forward(ctypes.byref(d.c()), _p(sched), _p(x), _p(gate), ctypes.byref(w), _p(y), _p(saved),
                                 _p(ws), _stream(stream)), "mok_moe_forward")
 
 
-def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws, stream=None):
-    w = _Weights(w1.data_ptr(), w2.data_ptr())
+def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws, stream=None,
+                 mxw: Optional[MxWeights] = None):
+    w, _keep = _weights(w1, w2, mxw)
     _check(_lib.mok_moe_backward(ctypes.byref(d.c()), _p(sched), _p(x), _p(idx), _p(gate), ctypes.byref(w), _p(wr),
                                  _p(saved), _p(dy), _p(dx), _p(dw1), _p(dw2), _p(dgate), _p(dwr), _p(ws),
                                  _stream(stream)), "mok_moe_backward")
@@ -266,11 +313,59 @@ class Buffers:
         return dict(a=au[:, : d.I], u=au[:, d.I:], h=h)
 
 
-def step(d: Desc, buf: Buffers, x, wr, bias, w1, w2, dy=None, stream=None, router_grad=True):
+def step(d: Desc, buf: Buffers, x, wr, bias, w1, w2, dy=None, stream=None, router_grad=True, mxw=None):
     """route -> schedule -> forward (-> backward): one layer step, all on the GPU."""
     route(d, x, wr, bias, buf.idx, buf.gate, None, stream)
     schedule_build(d, buf.idx, buf.sched, stream)
-    moe_forward(d, buf.sched, x, buf.gate, w1, w2, buf.y, buf.saved, buf.fwd_ws, stream)
+    moe_forward(d, buf.sched, x, buf.gate, w1, w2, buf.y, buf.saved, buf.fwd_ws, stream, mxw)
     if dy is not None:
         moe_backward(d, buf.sched, x, buf.idx, buf.gate, w1, w2, wr if router_grad else None, buf.saved, dy,
-                     buf.dx, buf.dw1, buf.dw2, buf.dgate, buf.dwr if router_grad else None, buf.bwd_ws, stream)
+                     buf.dx, buf.dw1, buf.dw2, buf.dgate, buf.dwr if router_grad else None, buf.bwd_ws, stream, mxw)
+
+
+class StreamedStep:
+    """Buffers and call sequence of one streamed MXFP8 step: d.mb_count micro-batches of
+    d.T tokens (x, dy are [mb_count*T, H]); route -> schedule -> forward for micro-batches
+    0..M-1, then backward for M-1..0, deferring the weight gradients to the last call."""
+
+    def __init__(self, d: Desc, device="cuda", wgrad_f32=False):
+        assert d.mx
+        self.d = d
+        M, T = d.mb_count, d.T
+        sz = workspace_query(d)
+        u8 = dict(dtype=torch.uint8, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.sched = [torch.empty(max(sz["sched"], 256), **u8) for _ in range(M)]
+        self.saved = [torch.empty(max(sz["saved"], 256), **u8) for _ in range(M)]
+        self.fwd_ws = torch.empty(max(sz["fwd_ws"], 256), **u8)
+        self.bwd_ws = torch.empty(max(sz["bwd_ws"], 256), **u8)
+        self.idx = torch.empty(M * T, d.k, dtype=torch.int32, device=device)
+        self.gate = torch.empty(M * T, d.k, **f32)
+        self.dgate = torch.empty(M * T, d.k, **f32)
+        self.y = torch.empty(M * T, d.H, dtype=torch.bfloat16, device=device)
+        self.dx = torch.empty(M * T, d.H, dtype=torch.bfloat16, device=device)
+        wdt = torch.float32 if wgrad_f32 else torch.bfloat16
+        self.dw1 = torch.empty(d.E, 2 * d.I, d.H, dtype=wdt, device=device)
+        self.dw2 = torch.empty(d.E, d.H, d.I, dtype=wdt, device=device)
+        self.dwr = torch.empty(d.E, d.H, dtype=wdt, device=device)
+
+    def desc(self, m: int, defer: bool = False) -> Desc:
+        from dataclasses import replace
+        return replace(self.d, mb_index=m, flags=self.d.flags | (FLAG_WGRAD_DEFER if defer else 0))
+
+    def run(self, x, wr, bias, mxw: MxWeights, dy=None, stream=None, router_grad=True):
+        d, M, T = self.d, self.d.mb_count, self.d.T
+        sl = lambda t, m: t[m * T:(m + 1) * T]
+        for m in range(M):
+            dm = self.desc(m)
+            route(dm, sl(x, m), wr, bias, sl(self.idx, m), sl(self.gate, m), None, stream)
+            schedule_build(dm, sl(self.idx, m), self.sched[m], stream)
+            moe_forward(dm, self.sched[m], sl(x, m), sl(self.gate, m), None, None, sl(self.y, m), self.saved[m],
+                        self.fwd_ws, stream, mxw)
+        if dy is None:
+            return
+        for m in reversed(range(M)):
+            dm = self.desc(m, defer=m > 0)
+            moe_backward(dm, self.sched[m], sl(x, m), sl(self.idx, m), sl(self.gate, m), None, None,
+                         wr if router_grad else None, self.saved[m], sl(dy, m), sl(self.dx, m), self.dw1, self.dw2,
+                         sl(self.dgate, m), self.dwr if router_grad else None, self.bwd_ws, stream, mxw)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(mok):
     for n in _declared():
         assert hasattr(lib, n), n
     assert set(_declared()) == set(mok.EXPORTS)
-    assert mok.version() == 100
+    assert mok.version() == 200
 
 
 def test_status_strings(mok):
@@ -52,7 +52,10 @@ def _d(mok, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), 3), (dict(k=9), 3), (dict(E=0), 3), (dict(E=1025), 3), (dict(k=17, E=32), 3),
     (dict(H=100), 3), (dict(I=96), 3), (dict(T=-1), 3), (dict(tile_m=48), 3), (dict(grid=-2), 3),
-    (dict(act=2), 4), (dict(act=1, gemm=2), 4), (dict(T=1 << 29, k=8), 3),
+    (dict(act=2), 4), (dict(act=0, gemm=2), 4), (dict(T=1 << 29, k=8), 3),
+    (dict(flags=2), 4), (dict(mb_count=2), 3), (dict(gemm=2, mb_count=2, mb_index=2), 3),
+    (dict(gemm=2, mb_index=-1), 3), (dict(gemm=2, mb_count=-1), 3), (dict(gemm=2, ring=-1), 3),
+    (dict(gemm=2, T=1 << 20, H=4096, E=8, k=8, mb_count=64), 3),
 ])
 def test_descriptor_validation(mok, kw, status):
     with pytest.raises(mok.MokError) as ei:
@@ -72,6 +75,21 @@ def test_workspace_sizes_cover_worst_case(mok):
     assert lay["h_offset"] >= 2 * R * 2 * d.I and lay["h_offset"] % 256 == 0
 
 
+def test_mxfp8_workspace_sizes(mok):
+    """MXFP8: ring slots of quantised rows and partials, the stash of every micro-batch,
+    and the token-axis operands padded to 128 rows per expert."""
+    for M, S in ((1, 1), (8, 2)):
+        d = _d(mok, T=256, H=256, E=8, k=2, I=128, gemm=mok.MXFP8, mb_count=M, ring=S)
+        s = mok.workspace_query(d)
+        R = d.R
+        assert s["fwd_ws"] >= S * (d.T * d.H * 33 // 32 + R * d.I * 33 // 32 + 2 * R * d.H)
+        stash = M * R * (2 * d.H + 2 * d.H + 2 * d.I + 4 * d.I + 8)
+        kmax = M * R + 128 * d.E
+        flush = kmax * (2 * d.H + d.I + 2 * d.I) * 33 // 32 + 4 * kmax
+        assert s["bwd_ws"] >= S * (d.T * d.H + R * 2 * d.I + 2 * R * d.H) + stash + flush
+        assert s["saved"] == mok.workspace_query(_d(mok, T=256, H=256, E=8, k=2, I=128))["saved"]
+
+
 def test_null_and_alignment_rejected_before_launch(mok):
     d = _d(mok)
     lib = mok._lib
@@ -89,3 +107,22 @@ def test_null_and_alignment_rejected_before_launch(mok):
     assert st == 1
     st = lib.mok_moe_forward(ctypes.byref(c), ctypes.c_void_p(4096), None, None, None, None, None, None, None)
     assert st == 1
+    # MXFP8: weights_quantize needs gemm = MXFP8 and every output pointer
+    q = mok._MxWeights(*([4096] * 8))
+    st = lib.mok_weights_quantize(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.byref(q),
+                                  None)
+    assert st == 4
+    cm = _d(mok, gemm=mok.MXFP8).c()
+    q.w1ts = None
+    st = lib.mok_weights_quantize(ctypes.byref(cm), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.byref(q),
+                                  None)
+    assert st == 1
+    q.w1ts = 4100
+    st = lib.mok_weights_quantize(ctypes.byref(cm), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.byref(q),
+                                  None)
+    assert st == 2
+    # MXFP8 forward without the quantised weights
+    w = mok._Weights(4096, 4096, None)
+    st = lib.mok_moe_forward(ctypes.byref(cm), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                             ctypes.byref(w), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None)
+    assert st in (1, 5)

@@ -1,0 +1,196 @@
+"""GPU parity of the MXFP8 path (E4M3 elements, E8M0 scale per 32 along each GEMM's K).
+
+* the weight quantisers (four orientations) against the oracle's quantiser, bit for bit,
+  on weights with planted edge blocks (all zero, 2^+-40 magnitudes, saturation, ties);
+* one MXFP8 layer step (route, schedule, forward, backward) against the oracle's MXFP8
+  step, which quantises every GEMM operand at the same points: rel. Frobenius <= 2e-2;
+* the streamed step (micro-batches through the ring, weight gradients deferred to the
+  last backward call) bit-identical to one call over the whole batch;
+* repeated steps bit-identical; an empty batch still writes zero weight gradients.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from harness import np64, rel_fro
+from mixture_experts_layer_stable_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_MX = 2e-2
+DEV = "cuda"
+
+
+def _mok():
+    from mixture_experts_layer_stable_amd import mok
+    return mok
+
+
+def _decode_e4m3(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.float8_e4m3fn).double().numpy()
+
+
+def _edge_weights(E, rows, cols, seed):
+    """bf16 weights with random per-block magnitudes and planted special blocks."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((E, rows, cols)) * np.exp2(rng.integers(-40, 41, (E, rows // 32, 1, cols // 32, 1))
+                                                      ).repeat(32, 2).repeat(32, 4).reshape(E, rows, cols)
+    w[0, :32, :32] = 0.0                                  # all-zero block (both orientations)
+    w[0, 32:64, :] *= 2.0**-120                           # tiny: scale clamps at 2^-127
+    w[-1, -32:, -32:] = 1.9 * 2.0**10                     # 1.9 * 2^10: elements 1.9 * 2^8 -> saturate to 448
+    w[-1, -1, -1] = 2.0**10                               # block max sets the scale
+    w[1, 5, :] = 2.0**-9 * 3 * (1 + (np.arange(cols) % 2))  # subnormal ties under a large block max
+    return torch.from_numpy(w).to(torch.bfloat16)
+
+
+def test_weights_quantize_bit_exact():
+    mok = _mok()
+    E, H, I = 3, 256, 128
+    d = mok.Desc(64, H, E, 2, I, act=mok.BF16, gemm=mok.MXFP8)
+    w1 = _edge_weights(E, 2 * I, H, 1)
+    w2 = _edge_weights(E, H, I, 2)
+    q = mok.MxWeights(d, DEV)
+    mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
+    torch.cuda.synchronize()
+    W1 = w1.double().numpy()
+    W2 = w2.double().numpy()
+    cases = {
+        "w1": (q.w1q, q.w1s, W1, -1),                                  # [E][2I][H] along H
+        "w2": (q.w2q, q.w2s, W2, -1),                                  # [E][H][I] along I
+        "w2t": (q.w2tq, q.w2ts, np.swapaxes(W2, 1, 2), -1),            # [E][I][H] along H
+        "w1t": (q.w1tq, q.w1ts, np.swapaxes(W1, 1, 2), -1),            # [E][H][2I] along 2I
+    }
+    for name, (tq, ts, ref, ax) in cases.items():
+        el, s = orc.mx.mx_quantize(ref, ax)
+        got_s = ts.cpu().numpy().astype(np.int64) - 127
+        np.testing.assert_array_equal(got_s, s, err_msg=name + " scales")
+        np.testing.assert_array_equal(_decode_e4m3(tq), el, err_msg=name + " elements")
+
+
+# ---------------------------------------------------------------------------------------
+
+def _case(w):
+    x = inputs.make_x(w)
+    dy = inputs.make_dy(w)
+    wr = inputs.make_wr(w)
+    b = inputs.make_bias(w)
+    w1 = torch.stack([inputs.make_w1(w, e) for e in range(w.E)])
+    w2 = torch.stack([inputs.make_w2(w, e) for e in range(w.E)])
+    return x, dy, wr, b, w1, w2
+
+
+def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True):
+    mok = _mok()
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m)
+    buf = mok.Buffers(d, DEV)
+    q = mok.MxWeights(d, DEV)
+    w1d, w2d = w1.to(DEV), w2.to(DEV)
+    mok.weights_quantize(d, w1d, w2d, q)
+    xd, dyd, wrd = x.to(DEV), dy.to(DEV), wr.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    mok.step(d, buf, xd, wrd, bd, None, None, dyd, router_grad=router_grad, mxw=q)
+    torch.cuda.synchronize()
+    out = dict(idx=buf.idx.cpu().numpy(), gate=buf.gate.cpu(), y=buf.y.cpu(), dx=buf.dx.cpu(),
+               dgate=buf.dgate.cpu(), dw1=buf.dw1.cpu(), dw2=buf.dw2.cpu(), perm=buf.schedule_views()["perm"].cpu())
+    if router_grad:
+        out["dwr"] = buf.dwr.cpu()
+    sv = buf.saved_views()
+    out.update(a=sv["a"].cpu(), u=sv["u"].cpu(), h=sv["h"].cpu())
+    return out
+
+
+def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0):
+    mok = _mok()
+    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m, mb_count=M, ring=ring)
+    st = mok.StreamedStep(d, DEV)
+    q = mok.MxWeights(d, DEV)
+    mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
+    st.run(x.to(DEV), wr.to(DEV), None if b is None else b.to(DEV), q, dy.to(DEV))
+    torch.cuda.synchronize()
+    return dict(idx=st.idx.cpu().numpy(), gate=st.gate.cpu(), y=st.y.cpu(), dx=st.dx.cpu(), dgate=st.dgate.cpu(),
+                dw1=st.dw1.cpu(), dw2=st.dw2.cpu(), dwr=st.dwr.cpu())
+
+
+def _oracle(w, x, dy, wr, b, w1, w2):
+    xs, dys, wrs = x.float().numpy(), dy.float().numpy(), wr.float().numpy()
+    z, idx, g = orc.route(xs, wrs, w.k, None if b is None else b.numpy())
+    W = orc.DenseWeights(w1.float().numpy(), w2.float().numpy())
+    f = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I)
+    bw = orc.mx.backward_mx(xs, W, wrs, idx, g, f, dys, w.I)
+    return idx, g, f, bw
+
+
+MX_CASES = {
+    "small": inputs.replace(inputs.WORKLOADS["small_bf16"], gemm="mxfp8"),
+    "imbalanced": inputs.replace(inputs.WORKLOADS["imbalanced_bf16"], gemm="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name,tile_m", [("small", 0), ("imbalanced", 0), ("imbalanced", 32), ("small", 64)])
+def test_mx_step_parity(name, tile_m):
+    w = MX_CASES[name]
+    print("case", name, "tile_m", tile_m, flush=True)
+    x, dy, wr, b, w1, w2 = _case(w)
+    g = _run_whole(w, x, dy, wr, b, w1, w2, tile_m=tile_m)
+    idx, gate, f, bw = _oracle(w, x, dy, wr, b, w1, w2)
+    np.testing.assert_array_equal(g["idx"], idx)
+    perm = g["perm"].numpy()
+    errs = {
+        "gate": rel_fro(g["gate"].numpy(), gate),
+        "y": rel_fro(np64(g["y"]), f["y"]),
+        "a": rel_fro(np64(g["a"]), f["a"][perm]),
+        "u": rel_fro(np64(g["u"]), f["u"][perm]),
+        "h": rel_fro(np64(g["h"]), f["h"][perm]),
+        "dx": rel_fro(np64(g["dx"]), bw["dx"]),
+        "dgate": rel_fro(g["dgate"].numpy(), bw["dgate"]),
+        "dw1": rel_fro(np64(g["dw1"]), np.stack([bw["dw1"][e] for e in range(w.E)])),
+        "dw2": rel_fro(np64(g["dw2"]), np.stack([bw["dw2"][e] for e in range(w.E)])),
+        "dwr": rel_fro(np64(g["dwr"]), bw["dwr"]),
+    }
+    print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_MX, (k, v)
+
+
+def test_mx_streamed_equals_whole_batch():
+    """4 micro-batches through a 2-slot ring, backward 3..0 with dW deferred, against
+    one call over all 2048 tokens: every output bit-identical."""
+    w = MX_CASES["imbalanced"]
+    x, dy, wr, b, w1, w2 = _case(w)
+    whole = _run_whole(w, x, dy, wr, b, w1, w2, tile_m=64)
+    st = _run_streamed(w, 4, 2, x, dy, wr, b, w1, w2, tile_m=64)
+    np.testing.assert_array_equal(st["idx"], whole["idx"])
+    for n in ("gate", "y", "dx", "dgate", "dw1", "dw2", "dwr"):
+        a, c = st[n], whole[n]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           c.view(torch.int16) if c.dtype == torch.bfloat16 else c), n
+
+
+def test_mx_repeat_bit_identical():
+    w = inputs.replace(MX_CASES["small"], T=512)
+    x, dy, wr, b, w1, w2 = _case(w)
+    r1 = _run_whole(w, x, dy, wr, b, w1, w2)
+    r2 = _run_whole(w, x, dy, wr, b, w1, w2)
+    for n in ("y", "dx", "dgate", "dw1", "dw2", "dwr"):
+        assert torch.equal(r1[n].view(torch.int16) if r1[n].dtype == torch.bfloat16 else r1[n],
+                           r2[n].view(torch.int16) if r2[n].dtype == torch.bfloat16 else r2[n]), n
+
+
+def test_mx_empty_batch_writes_zero_weight_gradients():
+    mok = _mok()
+    E, H, I = 4, 256, 128
+    d = mok.Desc(0, H, E, 2, I, act=mok.BF16, gemm=mok.MXFP8)
+    buf = mok.Buffers(d, DEV)
+    q = mok.MxWeights(d, DEV)
+    w1 = torch.randn(E, 2 * I, H, device=DEV).to(torch.bfloat16)
+    w2 = torch.randn(E, H, I, device=DEV).to(torch.bfloat16)
+    mok.weights_quantize(d, w1, w2, q)
+    for t in (buf.dw1, buf.dw2, buf.dwr):
+        t.fill_(float("nan"))
+    x = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    wr = torch.randn(E, H, device=DEV).to(torch.bfloat16)
+    mok.step(d, buf, x, wr, None, None, None, x, mxw=q)
+    torch.cuda.synchronize()
+    for t in (buf.dw1, buf.dw2, buf.dwr):
+        assert torch.all(t == 0)
