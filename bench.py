@@ -8,6 +8,12 @@ tensors of the workload's shapes, resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config kimi_k2_bf16]
 
+With --config kimi_k2_mxfp8_stream a step is the streamed MXFP8 step: 8 micro-batches
+of 2048 tokens (route, schedule, forward for 0..7, then backward for 7..0 through a
+2-slot ring, weight gradients deferred to the last call). The expert weights are
+quantised to their four MXFP8 orientations once, before timing (a per-weight-update
+cost); activation and gradient quantisation is inside the step.
+
 Prints one JSON line. Runs on one GPU only; --gpus N > 1 exits with a message.
 """
 import argparse
@@ -22,17 +28,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; grouped-GEMM MFMA util %"
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 GEMMS = ("fc1", "fc2", "dh", "dx", "dw2", "dw1")
 
 
-def kernel_work(w, name):
-    """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes)."""
-    R, H, I, T, E = w.R, w.H, w.I, w.T, w.E
+def launch_flops(w, name):
+    """Flops of one launch of an expert GEMM (row GEMMs: one micro-batch; dW: the step)."""
+    M = max(1, w.micro_batches)
+    R = (w.T // M) * w.k
+    per_row = {"fc1": 4, "fc2": 2, "dh": 2, "dx": 4, "dw2": 2 * M, "dw1": 4 * M}[name]
+    return per_row * R * w.H * w.I
+
+
+def launches_per_step(w, name):
+    return 1 if name.startswith("dw") else max(1, w.micro_batches)
+
+
+def kernel_work(w, name, active_experts=None):
+    """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes).
+
+    Row GEMMs and the bandwidth kernels process one micro-batch per launch (the whole
+    batch when there is one); the weight-gradient GEMMs process the whole step. For the
+    MXFP8 row GEMMs the bound is the larger of flops / 5 PFLOP/s and bytes / 8 TB/s,
+    bytes = the E4M3+E8M0 weights of the experts with rows (read once) plus the
+    activation rows read and written."""
+    M = max(1, w.micro_batches)
+    T, H, I, E = w.T // M, w.H, w.I, w.E
+    R = T * w.k
     es = 4 if w.act == "f32" else 2
-    flops = {"fc1": 4 * R * H * I, "fc2": 2 * R * H * I, "dh": 2 * R * H * I, "dx": 4 * R * H * I,
-             "dw2": 2 * R * H * I, "dw1": 4 * R * H * I}
+    flops = {k: launch_flops(w, k) for k in GEMMS}
+    if w.gemm == "mxfp8" and name in ("fc1", "fc2", "dh", "dx"):
+        q = 33.0 / 32.0  # E4M3 byte + one scale byte per 32
+        ae = E if active_experts is None else active_experts
+        wbytes = {"fc1": 2 * I * H, "fc2": H * I, "dh": I * H, "dx": H * 2 * I}[name] * q * ae
+        act = {"fc1": T * H * q + R * (2 * I * 2 + I * 2 + I * q),
+               "fc2": R * I * q + R * H * 2,
+               "dh": T * H * q + R * (2 * I * 2 + I * 2 + 4) + R * (2 * I * 2 + 2 * I * q),
+               "dx": R * 2 * I * q + R * H * 2}[name]
+        b = wbytes + act
+        if b / (HBM_PEAK_GBS * 1e9) > flops[name] / (MFMA_PEAK_TFLOPS["mxfp8"] * 1e12):
+            return "hbm", b
+        return "mfma", flops[name]
     if name in flops:
         return "mfma", flops[name]
     nbytes = {"combine": R * H * es + T * H * es + 4 * R,
@@ -126,8 +163,12 @@ def cpu_baseline(w, ntok, kept):
     W = KeptWeights(kept)
     t0 = time.perf_counter()
     _, idx, g = oracle.route(x, wr, w.k, b)
-    fwd = oracle.forward(x, W, idx, g, w.act, w.E, w.I)
-    oracle.backward(x, W, wr, idx, g, fwd, dy, w.act, w.I)
+    if w.gemm == "mxfp8":
+        fwd = oracle.mx.forward_mx(x, W, idx, g, w.E, w.I)
+        oracle.mx.backward_mx(x, W, wr, idx, g, fwd, dy, w.I)
+    else:
+        fwd = oracle.forward(x, W, idx, g, w.act, w.E, w.I)
+        oracle.backward(x, W, wr, idx, g, fwd, dy, w.act, w.I)
     dt = time.perf_counter() - t0
     blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     cores = max(blas, len(os.sched_getaffinity(0)))
@@ -142,6 +183,7 @@ def main():
     ap.add_argument("--config", default="kimi_k2_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-m", type=int, default=0, help="schedule tile rows (0 = two-wave rule)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (known bytes, for HBM counter scaling)")
     args = ap.parse_args()
@@ -154,9 +196,7 @@ def main():
     from mixture_experts_layer_stable_amd import inputs, mok
 
     w = inputs.WORKLOADS[args.config]
-    if w.gemm == "mxfp8":
-        print("workload %s (MXFP8 expert GEMMs) is not implemented by this version" % w.name, file=sys.stderr)
-        sys.exit(2)
+    mx = w.gemm == "mxfp8"
     torch.cuda.set_device(0)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.calibrate_copy:
@@ -166,25 +206,41 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 512, "imbalanced_bf16": 512}.get(w.name, 6)
+    ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 512, "imbalanced_bf16": 512,
+                               "kimi_k2_mxfp8_stream": 1}.get(w.name, 6)
     keep = cpu_sample_plan(w, ntok) if not args.no_cpu_baseline else []
     t0 = time.time()
     x, dy, wr, bias, w1, w2, kept = make_inputs(w, set(keep))
     torch.cuda.synchronize()
     log("inputs ready in %.1f s" % (time.time() - t0))
 
-    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act])
-    buf = mok.Buffers(d, "cuda", backward=True)
+    if mx:
+        M = w.micro_batches
+        d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=args.tile_m, mb_count=M,
+                     ring=2)
+        q = mok.MxWeights(d, "cuda")
+        mok.weights_quantize(d, w1, w2, q)
+        torch.cuda.synchronize()
+        del w1, w2
+        w1 = w2 = None
+        torch.cuda.empty_cache()
+        st = mok.StreamedStep(d, "cuda")
 
-    def step():
-        mok.step(d, buf, x, wr, bias, w1, w2, dy=dy)
+        def step():
+            st.run(x, wr, bias, q, dy)
+    else:
+        d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=args.tile_m)
+        buf = mok.Buffers(d, "cuda", backward=True)
+
+        def step():
+            mok.step(d, buf, x, wr, bias, w1, w2, dy=dy)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # per-kernel breakdown from one traced (untimed) step
-    with mok.KernelTrace("*", 64) as tr:
+    with mok.KernelTrace("*", 512) as tr:
         step()
     per = {}
     for name, ms in tr.durations_ms():
@@ -195,7 +251,7 @@ def main():
     # timed region; the dominant kernel's launches are bracketed by HIP events on its stream
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with mok.KernelTrace(dominant, capacity=max(4 * args.steps, 8)) as trd:
+    with mok.KernelTrace(dominant, capacity=max(16 * args.steps, 8)) as trd:
         start.record()
         for _ in range(args.steps):
             step()
@@ -205,9 +261,16 @@ def main():
     dom = [ms for _, ms in trd.durations_ms()]
     dom_ms = sum(dom) / len(dom)
 
-    bound, work = kernel_work(w, dominant)
+    active = None
+    if mx:  # experts with rows, averaged over the micro-batches (weights read by the row GEMMs)
+        from mixture_experts_layer_stable_amd.mok import schedule_layout_query
+        Ls = schedule_layout_query(d)
+        active = sum(int((s[Ls["counts"]: Ls["counts"] + 4 * w.E].view(torch.int32) > 0).sum()) for s in st.sched)
+        active /= len(st.sched)
+    gdt = w.gemm if mx else w.act
+    bound, work = kernel_work(w, dominant, active)
     if bound == "mfma":
-        peak = MFMA_PEAK_TFLOPS[w.act]
+        peak = MFMA_PEAK_TFLOPS[gdt]
         achieved = work / (dom_ms * 1e-3) / 1e12
         unit = "TFLOP/s"
     else:
@@ -216,8 +279,8 @@ def main():
         unit = "GB/s"
     traffic = measured_traffic(dominant, w.name)
     gemm_ms = sum(per.get(k, 0.0) for k in GEMMS)
-    gemm_flops = sum(kernel_work(w, k)[1] for k in GEMMS)
-    mfma_util = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (MFMA_PEAK_TFLOPS[w.act] * 1e12) if gemm_ms else None
+    gemm_flops = sum(launches_per_step(w, k) * launch_flops(w, k) for k in GEMMS)
+    mfma_util = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (MFMA_PEAK_TFLOPS[gdt] * 1e12) if gemm_ms else None
 
     result = {
         "metric": METRIC,
@@ -230,10 +293,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.act,
+        "dtype": gdt,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
-                   "routing": "zipf-imbalanced" if w.zipf else "near-uniform"},
+                   "routing": "zipf-imbalanced" if w.zipf else "near-uniform", "tile_m": d.c().tile_m or "auto",
+                   **({"micro_batches": w.micro_batches, "ring_slots": 2} if mx else {})},
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},
         "gemm_mfma_util_pct": mfma_util,
@@ -241,13 +305,13 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        del x, dy, w1, w2, buf
+        del x, dy, w1, w2
         torch.cuda.empty_cache()
         dt, cores, rows = cpu_baseline(w, ntok, kept)
         result["cpu_baseline"] = {
             "value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "first %d of %d tokens (%d routed rows): oracle route + forward + backward, %.1f s" % (
-                ntok, w.T, rows, dt)}
+            "sample": "first %d of %d tokens (%d routed rows): oracle%s route + forward + backward, %.1f s" % (
+                ntok, w.T, rows, " MXFP8" if mx else "", dt)}
     print(json.dumps(result), flush=True)
 
 

@@ -91,9 +91,10 @@ def mx_token_blocks(rows, seg_lengths):
     return out
 
 
-def forward_mx(x, weights, idx, gate, E: int, I: int) -> dict:
+def forward_mx(x, weights, idx, gate, E: int, I: int, experts=None) -> dict:
     """MXFP8 expert GEMMs, bf16 storage: same outputs as moe.forward(fmt='bf16') with
-    every GEMM operand quantised along its K."""
+    every GEMM operand quantised along its K. ``experts`` restricts the work to a subset
+    of experts (other slots stay NaN and y is not formed)."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     k = idx.shape[1]
@@ -102,7 +103,9 @@ def forward_mx(x, weights, idx, gate, E: int, I: int) -> dict:
     u_s = np.full((R, I), np.nan)
     h_s = np.full((R, I), np.nan)
     p = np.full((R, H), np.nan)
-    for e, s in enumerate(_slots_by_expert(idx, E)):
+    by_e = _slots_by_expert(idx, E)
+    for e in (range(E) if experts is None else experts):
+        s = by_e[e]
         if s.size == 0:
             continue
         X = mx(x[s // k])
@@ -112,6 +115,8 @@ def forward_mx(x, weights, idx, gate, E: int, I: int) -> dict:
         Hh = bf16_round(silu(A) * U)
         O = mx(Hh) @ mx(weights.w2(e)).T
         a_s[s], u_s[s], h_s[s], p[s] = bf16_round(A), bf16_round(U), Hh, bf16_round(O)
+    if experts is not None:
+        return dict(a=a_s, u=u_s, h=h_s, p=p)
     g = np.asarray(gate, np.float64)
     y = np.zeros((T, H))
     for j in range(k):
@@ -119,9 +124,11 @@ def forward_mx(x, weights, idx, gate, E: int, I: int) -> dict:
     return dict(a=a_s, u=u_s, h=h_s, p=p, y=bf16_round(y))
 
 
-def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True) -> dict:
+def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True, experts=None) -> dict:
     """Gradients with MXFP8 expert GEMMs. `segments[e]` lists the lengths of expert e's
-    row segments in slot order (one per micro-batch; default: one segment)."""
+    row segments in slot order, token blocks restarting at each (default: one segment,
+    the expert's rows of the whole step). ``experts`` restricts the work to a subset of
+    experts: only their d-gates, dGU, partial rows and weight gradients are formed."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     g = np.asarray(gate, np.float64)
@@ -135,7 +142,8 @@ def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, route
     q = np.full((R, H), np.nan)
     dw1, dw2 = {}, {}
     by_e = _slots_by_expert(idx, E)
-    for e, s in enumerate(by_e):
+    for e in (range(E) if experts is None else experts):
+        s = by_e[e]
         if s.size == 0:
             dw1[e], dw2[e] = np.zeros((2 * I, H)), np.zeros((H, I))
             continue
@@ -155,6 +163,8 @@ def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, route
         dO = bf16_round(gf[s][:, None] * dy[t])
         dw2[e] = bf16_round(mx_token_blocks(dO, seg).T @ mx_token_blocks(hh, seg))
         dw1[e] = bf16_round(mx_token_blocks(G, seg).T @ mx_token_blocks(x[t], seg))
+    if experts is not None:
+        return dict(dgate=gp.reshape(T, k), dgu=dgu, dw1=dw1, dw2=dw2, q=q)
     gpk = gp.reshape(T, k)
     ssum = np.zeros(T)
     for j in range(k):

@@ -136,3 +136,72 @@ def test_kimi_k2_full_size_near_uniform():
 def test_kimi_k2_full_size_zipf_imbalanced():
     """The streamed workload's inputs and Zipf bias, with bf16 expert GEMMs on the whole batch."""
     _run(inputs.replace(inputs.WORKLOADS["kimi_k2_mxfp8_stream"], gemm="bf16", micro_batches=1))
+
+
+def test_kimi_k2_mxfp8_streamed_full_size():
+    """The streamed MXFP8 workload at full size, in the launch configuration bench.py times:
+    8 micro-batches of 2048 tokens, 2-slot ring, Zipf routing, weight gradients deferred to
+    the last backward call. Routing of all 16384 tokens bit-exact; one sampled token's y,
+    dX and d-gates, and the whole dW1[e], dW2[e] of two of its experts (over all of their
+    rows of the step) against the oracle's MXFP8 step within 2e-2; a second step gives
+    the same bits."""
+    from mixture_experts_layer_stable_amd import mok
+    w = inputs.WORKLOADS["kimi_k2_mxfp8_stream"]
+    M = w.micro_batches
+    dev = "cuda"
+    rng = np.random.default_rng(4321)
+    x_cpu, wr_cpu, dy_cpu = inputs.make_x(w), inputs.make_wr(w), inputs.make_dy(w)
+    b = inputs.make_bias(w)
+    z, idx, g = orc.route(x_cpu.float().numpy(), wr_cpu.float().numpy(), w.k, b.numpy())
+    counts = np.bincount(idx.ravel(), minlength=w.E)
+    tok = np.array([int(rng.integers(w.T))])
+    exps = sorted(idx[tok[0]].tolist(), key=lambda e: counts[e])[:2]
+    need = set(idx[tok].ravel().tolist())
+    print("case mxfp8 stream T=%d M=%d token %d experts %s rows %s" % (w.T, M, tok[0], exps,
+          [int(counts[e]) for e in exps]), flush=True)
+
+    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, mb_count=M, ring=2)
+    q = mok.MxWeights(d, dev)
+    kept = {}
+    w1 = torch.empty(w.E, 2 * w.I, w.H, dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty(w.E, w.H, w.I, dtype=torch.bfloat16, device=dev)
+    for e in range(w.E):
+        a1, a2 = inputs.make_w1(w, e), inputs.make_w2(w, e)
+        w1[e].copy_(a1)
+        w2[e].copy_(a2)
+        if e in need:
+            kept[e] = (a1, a2)
+    mok.weights_quantize(d, w1, w2, q)
+    torch.cuda.synchronize()
+    del w1, w2
+    torch.cuda.empty_cache()
+    st = mok.StreamedStep(d, dev)
+    x, wr, dy, bias = x_cpu.to(dev), wr_cpu.to(dev), dy_cpu.to(dev), b.to(dev)
+    st.run(x, wr, bias, q, dy)
+    torch.cuda.synchronize()
+
+    np.testing.assert_array_equal(st.idx.cpu().numpy(), idx)
+    assert rel_fro(st.gate.cpu().numpy(), g) <= 1e-6
+
+    W = _Weights(kept)
+    xs, dys, wrs = x_cpu.float().numpy(), dy_cpu.float().numpy(), wr_cpu.float().numpy()
+    f = orc.mx.forward_mx(xs[tok], W, idx[tok], g[tok], w.E, w.I)
+    bw = orc.mx.backward_mx(xs[tok], W, wrs, idx[tok], g[tok], f, dys[tok], w.I)
+    errs = {"y": rel_fro(np64(st.y[tok]), f["y"]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"]),
+            "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"])}
+    for e in exps:
+        fe = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, experts=[e])
+        be = orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e])
+        errs["dw1[%d]" % e] = rel_fro(np64(st.dw1[e]), be["dw1"][e])
+        errs["dw2[%d]" % e] = rel_fro(np64(st.dw2[e]), be["dw2"][e])
+    print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= 2e-2, (k, v)
+
+    ref = {n: getattr(st, n).clone() for n in ("y", "dx", "dw1", "dw2", "dwr", "dgate")}
+    st.run(x, wr, bias, q, dy)
+    torch.cuda.synchronize()
+    for n, t in ref.items():
+        a = getattr(st, n)
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           t.view(torch.int16) if t.dtype == torch.bfloat16 else t), n

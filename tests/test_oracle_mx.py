@@ -355,3 +355,21 @@ def test_flush_dw_dgu_and_do_along_tokens():
         assert np.all(bm["dw1"][e][rows, HF // 2:] == 0), e
         assert np.all(bm["dw2"][e][:, IF // 2:] == 0), e
         assert np.any(bb["dw1"][e][rows, HF // 2:] != 0) and np.any(bb["dw2"][e][:, IF // 2:] != 0)
+
+
+def test_mx_expert_subset_matches_full_step():
+    """Restricting the MX step to some experts reproduces their slots of the full step."""
+    rng, x, dy, w1, w2 = _base(31)
+    wr = rng.standard_normal((EF, HF)) * 0.2
+    z, idx, g = orc.route(x, wr, 2, exact=True)
+    W = orc.DenseWeights(w1, w2)
+    f = mx.forward_mx(x, W, idx, g, EF, IF)
+    b = mx.backward_mx(x, W, wr, idx, g, f, dy, IF)
+    fe = mx.forward_mx(x, W, idx, g, EF, IF, experts=[1])
+    be = mx.backward_mx(x, W, wr, idx, g, fe, dy, IF, experts=[1])
+    s = np.nonzero(idx.ravel() == 1)[0]
+    for n in ("a", "u", "h", "p"):
+        np.testing.assert_array_equal(fe[n][s], f[n][s])
+    np.testing.assert_array_equal(be["dgate"].ravel()[s], b["dgate"].ravel()[s])
+    np.testing.assert_array_equal(be["dw1"][1], b["dw1"][1])
+    np.testing.assert_array_equal(be["dw2"][1], b["dw2"][1])
