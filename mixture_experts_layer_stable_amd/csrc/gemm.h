@@ -317,7 +317,10 @@ namespace mok {
 // Epilogue staging: each wave copies one (or a pair of) 32x32 accumulator
 // block(s) through its own LDS patch and hands them back with every lane
 // owning 16 consecutive columns of one row, so global accesses are 16-byte
-// vectors. Call after main_loop (smem is free); all waves must call it.
+// vectors. Call after main_loop (its final barrier frees smem). A wave only
+// touches its own patch and a wave's LDS operations execute in issue order, so
+// there is no workgroup barrier inside; a caller that shares LDS results across
+// waves afterwards (or reuses smem) synchronises itself.
 //   f(row, col, g, u): row/col are workgroup-tile coordinates of the first of
 //   the lane's 16 columns; g[16] = block fn values; u[16] = block fn+1 values
 //   when PAIR (the SwiGLU up half), otherwise unused.
@@ -338,7 +341,6 @@ __device__ __forceinline__ void epilogue16(f32x16_t (&acc)[Tl::FM][Tl::FN], char
         patch[row * kPatchLd + (lane & 31)] = acc[fm][fn][r];
         if constexpr (PAIR) patch[row * kPatchLd + 32 + (lane & 31)] = acc[fm][fn + 1][r];
       }
-      __syncthreads();
       const int row = lane >> 1, c0 = (lane & 1) * 16;
       float g[16], u[16];
 #pragma unroll
@@ -351,7 +353,6 @@ __device__ __forceinline__ void epilogue16(f32x16_t (&acc)[Tl::FM][Tl::FN], char
         }
       }
       f(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c0, g, u);
-      __syncthreads();
     }
 }
 

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs<T> a) {
       if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
     });
     // blocks in ascending column order: the result depends on BN only, not on the wave layout
+    __syncthreads();  // s_red from every wave
     for (int i = tid; i < t.nrows; i += kThreads) {
       float s = 0.0f;
 #pragma unroll

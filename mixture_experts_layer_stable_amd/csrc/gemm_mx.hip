@@ -278,6 +278,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
         const float blk = (lane & 1) ? other + part : part + other;
         if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
       });
+      __syncthreads();  // s_red from every wave
       for (int i = tid; i < t.nrows; i += Tl::NT) {
         float s = 0.0f;
 #pragma unroll
