@@ -247,4 +247,94 @@ __device__ __forceinline__ void main_loop2(const OA& oa, const OB& ob, int KT, c
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Split form of main_loop2 for kernels that pipeline across output tiles: the
+// prologue (first STAGES-1 K-tiles) of tile i+1 is issued before tile i's
+// epilogue, whose EXTRA global stores per wave are then younger than the prologue
+// DMAs. Vector-memory operations complete in issue order, so a wait for a prologue
+// tile may leave those stores outstanding; a wait for any later tile covers them.
+// ---------------------------------------------------------------------------
+template <int STAGES, class OA, class OB>
+__device__ __forceinline__ void ring_prologue(const OA& oa, const OB& ob, int KT, char* smem, int wave) {
+  constexpr int SB = OA::BYTES + OB::BYTES;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < KT) {
+      oa.issue(s, smem + s * SB, wave);
+      ob.issue(s, smem + s * SB + OA::BYTES, wave);
+    }
+  }
+}
+
+template <int N, int EXTRA>
+__device__ __forceinline__ void wait_vmcnt_extra(bool prologue_tile) {
+  if (prologue_tile) wait_vmcnt<N + EXTRA>(); else wait_vmcnt<N>();
+}
+
+template <class Tl, int STAGES, int EXTRA, class OA, class OB>
+__device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, char* smem, int wave, int lane,
+                                          f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  static_assert(STAGES == 3, "ring_loop waits are written for 3 stages");
+  constexpr int SB = OA::BYTES + OB::BYTES;
+  constexpr int NI = OA::NI + OB::NI;
+  constexpr int KS = OA::BK / 16;
+  zero_acc<Tl>(acc);
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool pro = kt < STAGES - 1;  // issued by ring_prologue, before the stores
+    if (kt + 1 < KT) wait_vmcnt_extra<NI, EXTRA>(pro); else wait_vmcnt_extra<0, EXTRA>(pro);
+    ring_barrier();
+    const int nk = kt + STAGES - 1;
+    if (nk < KT) {
+      char* st = smem + (nk % STAGES) * SB;
+      oa.issue(nk, st, wave);
+      ob.issue(nk, st + OA::BYTES, wave);
+    }
+    const char* cur = smem + (kt % STAGES) * SB;
+    uint4 a[2][Tl::FM], b[2][Tl::FN];
+#pragma unroll
+    for (int fm = 0; fm < Tl::FM; ++fm) a[0][fm] = oa.frag(cur, fm, 0);
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; ++fn) b[0][fn] = ob.frag(cur + OA::BYTES, fn, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int fm = 0; fm < Tl::FM; ++fm) a[c ^ 1][fm] = oa.frag(cur, fm, ks + 1);
+#pragma unroll
+        for (int fn = 0; fn < Tl::FN; ++fn) b[c ^ 1][fn] = ob.frag(cur + OA::BYTES, fn, ks + 1);
+      }
+#pragma unroll
+      for (int fm = 0; fm < Tl::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Tl::FN; ++fn) Mma<bf16>::run(acc[fm][fn], a[c][fm], b[c][fn]);
+    }
+  }
+  __syncthreads();
+}
+
+// bf16 epilogue through a per-wave patch of 32 rows x 40 bf16 (2560 bytes, outside
+// the ring): lane (row = lane/2, half = lane&1) stores 16 consecutive bf16 of a row of
+// each 32x32 block as two 16-byte vectors: FM*FN*2 global stores per lane.
+template <class Tl, class F>
+__device__ __forceinline__ void epilogue_bf16(f32x16_t (&acc)[Tl::FM][Tl::FN], char* patch, int wm, int wn, int lane,
+                                              F&& store) {
+  constexpr int PLD = 40;
+  uint16_t* p = reinterpret_cast<uint16_t*>(patch);
+#pragma unroll
+  for (int fm = 0; fm < Tl::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Tl::FN; ++fn) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        p[row * PLD + (lane & 31)] = (uint16_t)f32_to_bf16(acc[fm][fn][r]);
+      }
+      const int row = lane >> 1, c0 = (lane & 1) * 16;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(patch + (row * PLD + c0) * 2);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(patch + (row * PLD + c0 + 8) * 2);
+      store(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c0, v0, v1);
+    }
+}
+
 }  // namespace mok

@@ -196,6 +196,73 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
   });
 }
 
+// Weight gradients with bf16 output, persistent and pipelined across output tiles:
+// the ring prologue of the next tile is issued before this tile's epilogue, so the
+// epilogue's stores drain while the next tile's first K-tiles load. The workgroup
+// walks a contiguous range of the tile list (e, mt, nt), one range per XCD.
+template <class Tl>
+__global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E) {
+  using OA = OpMN<Tl::BM, 32, Tl::FM, Tl::NW>;
+  using OB = OpMN<Tl::BN, 32, Tl::FN, Tl::NW>;
+  constexpr int STAGES = 3;
+  constexpr int SB = OA::BYTES + OB::BYTES;
+  constexpr int PATCH = 32 * 40 * 2;
+  constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
+  __shared__ __align__(1024) char smem[STAGES * SB + Tl::NW * PATCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  char* patch = smem + STAGES * SB + wave * PATCH;
+  const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  const int64_t total = (int64_t)E * MT * NT;
+  const int P = min(8, (int)gridDim.x);
+  const int xcd = blockIdx.x % P;
+  const int nx = ((int)gridDim.x - xcd + P - 1) / P;
+  const int li = blockIdx.x / P;
+  const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
+  int64_t L = lo + li;
+  if (L >= hi) return;
+  OA oa;
+  OB ob;
+  int e = 0, mt = 0, nt = 0, KT = 0;
+  const auto setup = [&](int64_t l) {
+    e = __builtin_amdgcn_readfirstlane((int)(l / (MT * NT)));
+    const int rem = (int)(l - (int64_t)e * MT * NT);
+    mt = __builtin_amdgcn_readfirstlane(rem / NT);
+    nt = __builtin_amdgcn_readfirstlane(rem - mt * NT);
+    const int seg0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(a.counts[e]);
+    oa.init(a.arows + (int64_t)seg0 * a.lda + mt * Tl::BM, 2 * (int64_t)a.lda, cnt,
+            [&](int f) { return wm * Tl::WTM + f * 32; }, wave, lane);
+    ob.init(a.brows + (int64_t)seg0 * a.ldb + nt * Tl::BN, 2 * (int64_t)a.ldb, cnt,
+            [&](int f) { return wn * Tl::WTN + f * 32; }, wave, lane);
+    KT = (cnt + 31) / 32;
+  };
+  setup(L);
+  ring_prologue<STAGES>(oa, ob, KT, smem, wave);
+  bool first = true;
+  for (;;) {
+    f32x16_t acc[Tl::FM][Tl::FN];
+    if (first)
+      ring_loop<Tl, STAGES, 0>(oa, ob, KT, smem, wave, lane, acc);
+    else
+      ring_loop<Tl, STAGES, EXTRA>(oa, ob, KT, smem, wave, lane, acc);
+    bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
+    const int64_t Ln = L + nx;
+    if (Ln < hi) {
+      setup(Ln);
+      ring_prologue<STAGES>(oa, ob, KT, smem, wave);
+    }
+    epilogue_bf16<Tl>(acc, patch, wm, wn, lane, [&](int row, int col, const uint4& v0, const uint4& v1) {
+      bf16* p = out + (int64_t)row * a.N + col;
+      stg16(p, v0);
+      stg16(p + 8, v1);
+    });
+    if (Ln >= hi) break;
+    L = Ln;
+    first = false;
+  }
+}
+
 // ---------------------------------------------------------------------------
 static Sched sched_of2(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
 
@@ -278,6 +345,13 @@ static hipError_t dw_launch(const Ctx& c, const DwArgs2& a) {
 }
 
 static hipError_t dw_any2(const Ctx& c, const DwArgs2& a) {
+  if (!c.wgrad_f32 && a.M % 256 == 0 && a.N % 256 == 0) {
+    using Tl = Tiling<256, 256, 2, 4>;
+    const int64_t tiles = (int64_t)c.E * (a.M / 256) * (a.N / 256);
+    const int g = (int)std::min<int64_t>(c.grid > 0 ? c.grid : c.num_cu, std::max<int64_t>(tiles, 1));
+    hipLaunchKernelGGL((dw_gemm2_pipe_kernel<Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    return hipGetLastError();
+  }
   if (a.M % 256 == 0 && a.N % 256 == 0) return dw_launch<Tiling<256, 256, 2, 4>>(c, a);
   return dw_launch<Tiling<128, 128, 2, 2>>(c, a);
 }
