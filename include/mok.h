@@ -222,7 +222,8 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
  *   pull reverse-combine: dy rows gathered through perm into the dH GEMM;
  *   dA = dy_t.W2[e]; the gate gradient g'_s = <dA, h> (= <dy_t, o_s>) is
  *   formed in that GEMM's epilogue (SonicMoE-style fusion, dothoosh.com page,
- *   "Technical details"), reduced over N-tiles in fixed order;
+ *   "Technical details"), one partial per 32-column block of I, summed over
+ *   the blocks in ascending order;
  *   dh = g*dA; da = dh*u*sig(a)*(1 + a*(1 - sig(a))); du = dh*silu(a);
  *   dGU = [da, du] (rounded to `act`); push reverse-dispatch:
  *   q_s = dGU.W1[e] (rounded to `act`), dx_t = sum_j q_tj + sum_j dz_tj*wr[idx_tj];

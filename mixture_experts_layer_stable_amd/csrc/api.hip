@@ -114,7 +114,7 @@ Layout layout_of(const mok_desc* d, int BM) {
   o = 0;
   L.dgu = o; o = up(o + es * (size_t)R * 2 * d->I);
   L.bpart = o; o = up(o + es * (size_t)R * d->H);
-  L.dgp = o; o = up(o + 4 * (size_t)R * dh_ntiles(d->I));
+  L.dgp = o; o = up(o + 4 * (size_t)R * dgate_parts(d->I));
   L.dz = o; o = up(o + 4 * (size_t)R);
   // bf16: token rows in routed order for the weight-gradient GEMMs (x and g*dy)
   const size_t rows = d->act == MOK_BF16 ? es * (size_t)R * d->H : 0;
@@ -154,7 +154,7 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.dguq = o; o = up(o + (size_t)(R * 2 * I));
   L.dgus = o; o = up(o + (size_t)(R * 2 * I / 32));
   L.bpart = o; o = up(o + (size_t)(2 * R * H));
-  L.dgp = o; o = up(o + (size_t)(4 * R * dh_ntiles(d->I)));
+  L.dgp = o; o = up(o + (size_t)(4 * R * dgate_parts(d->I)));
   L.bslot = o;
   o = (size_t)S * L.bslot;
   L.st_counts = o; o = up(o + (size_t)(4 * M * E));
@@ -210,6 +210,7 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
   c->max_tiles = L.max_tiles;
   c->num_cu = cus;
   c->grid = d->grid;
+  c->gemm = d->gemm;
   c->s = (hipStream_t)stream;
   c->counts = (int32_t*)(sb + L.counts);
   c->offsets = (int32_t*)(sb + L.offsets);

@@ -1,7 +1,7 @@
 // Bandwidth-bound kernels of the layer step, all with fixed summation orders.
 //
 //  combine     y_t = sum_{j=0..k-1} g_tj * partial[t*k+j]            (push combine)
-//  router_bwd  g'_tj = sum over dH N-tiles (ascending) of the d-gate partials;
+//  router_bwd  g'_tj = sum over the 32-column blocks of I (ascending) of the d-gate partials;
 //              dz_tj = g_tj * (g'_tj - sum_i g_ti g'_ti)   (softmax over the top k)
 //  dx_reduce   dx_t = sum_j q[t*k+j] + sum_j dz_tj * wr[idx_tj]  (push reverse-dispatch)
 //  dwr         dWr[e] = sum over e's routed rows (ascending slot) of dz_s * x_t
@@ -163,7 +163,7 @@ hipError_t launch_combine(const Ctx& c, const void* part, const float* gate, voi
 hipError_t launch_router_bwd(const Ctx& c, const float* dgp, const float* gate, float* dgate, float* dz) {
   if (c.T == 0) return hipSuccess;
   hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(c.T)), dim3(256), 0, c.s, dgp, gate, c.inv, dgate, dz, c.T,
-                     c.k, c.R, dh_ntiles(c.I));
+                     c.k, c.R, dgate_parts(c.I));
   return hipGetLastError();
 }
 

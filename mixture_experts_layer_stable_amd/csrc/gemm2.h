@@ -119,6 +119,47 @@ struct OpK {
 };
 
 // ---------------------------------------------------------------------------
+// K-contiguous operand with 32-element K-tiles: tile row = 64 bytes (4 chunks),
+// chunk c stored at position c ^ ((row >> 2) & 3), so the 16 rows a quarter-wave
+// reads (one chunk each) fall on 16 distinct 16-byte bank groups. One DMA
+// instruction fills 16 rows; lane l fetches the chunk that belongs at its slot.
+// ---------------------------------------------------------------------------
+template <int ROWS, int NF, int NW>
+struct OpK32 {
+  static constexpr int BK = 32;
+  static constexpr int BYTES = ROWS * 64;
+  static constexpr int NI = ROWS / (16 * NW);
+  static_assert(ROWS % (16 * NW) == 0, "rows");
+  const char* sbase;
+  uint32_t voff[NI];
+  uint32_t foff[NF][2];
+
+  template <class F, class G>
+  __device__ __forceinline__ void init(const void* sbase_, F rowoff, G frow, int wave, int lane) {
+    sbase = reinterpret_cast<const char*>(sbase_);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = 16 * (wave + NW * j) + (lane >> 2);
+      voff[j] = rowoff(row) + 16u * (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = frow(f) + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) foff[f][ks] = row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3));
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
+    const char* b = uniform_ptr(sbase + (int64_t)kt * 64);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) dma16_sv(b, voff[j], stage + (wave + NW * j) * 1024);
+  }
+  __device__ __forceinline__ uint4 frag(const char* stage, int f, int ks) const {
+    return *reinterpret_cast<const uint4*>(stage + foff[f][ks]);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // MN-contiguous operand, BK k-rows x ROWS bf16 per stage. Row k of the whole
 // operand starts at sbase + k * ld (bytes); rows k >= cnt read zeros (only the
 // last K-tile checks). NF fragments per k-step for this wave.

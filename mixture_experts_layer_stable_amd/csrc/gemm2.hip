@@ -27,10 +27,15 @@ constexpr int kMaxE2 = 1024;
 constexpr int kRowStages = 3;
 constexpr int kDwStages = 4;
 
-// Row GEMM wave layouts: 8 waves (2 per SIMD, 64x64 or 32x64 wave tiles) for
-// 64- and 128-row tiles; 4 waves for 32-row tiles (keeps gate/up block pairs).
+// Row GEMM wave layouts. 512-wide tiles (dh, dx, whose weights are read transposed
+// in 1 KB k-rows): 8 waves side by side (BM x 64 wave tiles, 32-element K-tiles), so
+// each LDS byte written by the DMA feeds twice the MFMA work of a 256-wide tile and
+// fragment reads per MFMA drop by a quarter. fc1/fc2 keep 256-wide tiles with 64-element
+// K-tiles: their weight rows are K-contiguous, and 32-element K-tiles would fetch them
+// 64 bytes at a time. 256/128-wide: 8 waves (2 x 4, 64x64 wave tiles) for 64/128-row
+// tiles, 4 waves for 32-row tiles.
 template <int BM, int BN>
-using RowTiling2 = Tiling<BM, BN, (BM == 32 ? 1 : 2), (BM == 32 ? 4 : 4)>;
+using RowTiling2 = Tiling<BM, BN, (BN == 512 || BM == 32 ? 1 : 2), (BN == 512 ? 8 : 4)>;
 
 struct RowArgs {
   Sched sc;
@@ -49,14 +54,15 @@ enum RowKind { FC1 = 0, FC2 = 1, DH = 2, DX = 3 };
 
 template <int KIND, class Tl>
 __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
-  using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
+  constexpr bool K32 = Tl::BN == 512;  // 32-element K-tiles
+  using OA = typename std::conditional<K32, OpK32<Tl::BM, Tl::FM, Tl::NW>, OpK<Tl::BM, Tl::FM, Tl::NW>>::type;
   constexpr bool B_MN = KIND == DH || KIND == DX;
-  using OB = typename std::conditional<B_MN, OpMN<Tl::BN, 64, Tl::FN, Tl::NW>, OpK<Tl::BN, Tl::FN, Tl::NW>>::type;
+  using OBK = typename std::conditional<K32, OpK32<Tl::BN, Tl::FN, Tl::NW>, OpK<Tl::BN, Tl::FN, Tl::NW>>::type;
+  using OB = typename std::conditional<B_MN, OpMN<Tl::BN, OA::BK, Tl::FN, Tl::NW>, OBK>::type;
   constexpr int SB = OA::BYTES + OB::BYTES;
   __shared__ __align__(1024) char smem[kRowStages * SB];
   __shared__ int s_ts[kMaxE2 + 1];
   __shared__ int s_slot[Tl::BM];
-  __shared__ float s_red[KIND == DH ? Tl::BN / 32 : 1][KIND == DH ? Tl::BM : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
               [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)(2 * a.I); }, frow_b, wave, lane);
     }
     f32x16_t acc[Tl::FM][Tl::FN];
-    main_loop2<Tl, kRowStages>(oa, ob, K / 64, smem, wave, wm, wn, lane, acc);
+    main_loop2<Tl, kRowStages>(oa, ob, K / OA::BK, smem, wave, wm, wn, lane, acc);
 
     if constexpr (KIND == FC1) {
       const int cbase = t.n * (Tl::BN / 2);
@@ -146,15 +152,11 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
         }
         const float other = __shfl_xor(part, 1);
         const float blk = (lane & 1) ? other + part : part + other;
-        if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+        // one partial per 32-column block of I: the sum over blocks (router_bwd, ascending)
+        // does not depend on the tile shape, the wave layout or the grid
+        if ((lane & 1) == 0 && row < t.nrows)
+          a.dgp[(int64_t)((t.n * Tl::BN + col) >> 5) * a.R + t.row0 + row] = blk;
       });
-      __syncthreads();  // s_red from every wave
-      for (int i = tid; i < t.nrows; i += Tl::NT) {
-        float s = 0.0f;
-#pragma unroll
-        for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
-        a.dgp[(int64_t)t.n * a.R + t.row0 + i] = s;
-      }
     }
   });
 }
@@ -278,12 +280,16 @@ static hipError_t row_launch(const Ctx& c, const RowArgs& a, int N) {
 
 template <int KIND, int BN>
 static hipError_t row_bm(const Ctx& c, const RowArgs& a, int N) {
-  switch (c.BM) {
-    case 32: return row_launch<KIND, 32, BN>(c, a, N);
-    case 64: return row_launch<KIND, 64, BN>(c, a, N);
-    case 128: return row_launch<KIND, 128, BN>(c, a, N);
+  if constexpr (BN == 512) {
+    return row_launch<KIND, 128, 512>(c, a, N);  // chosen only for 128-row tiles
+  } else {
+    switch (c.BM) {
+      case 32: return row_launch<KIND, 32, BN>(c, a, N);
+      case 64: return row_launch<KIND, 64, BN>(c, a, N);
+      case 128: return row_launch<KIND, 128, BN>(c, a, N);
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 static RowArgs row_args(const Ctx& c) {
@@ -323,7 +329,11 @@ hipError_t launch_dh_bf16(const Ctx& c, const void* dy, const void* w2, const vo
   a.h = (const bf16*)h;
   a.gate = gate;
   a.dgp = dgp;
-  return bn_rows(c.I) == 256 ? row_bm<DH, 256>(c, a, c.I) : row_bm<DH, 128>(c, a, c.I);
+  switch (bn_rows_bf16(c.I, c.BM)) {
+    case 512: return row_bm<DH, 512>(c, a, c.I);
+    case 256: return row_bm<DH, 256>(c, a, c.I);
+  }
+  return row_bm<DH, 128>(c, a, c.I);
 }
 
 hipError_t launch_dx_bf16(const Ctx& c, const void* dgu, const void* w1, void* part) {
@@ -331,7 +341,11 @@ hipError_t launch_dx_bf16(const Ctx& c, const void* dgu, const void* w1, void* p
   a.a = (const bf16*)dgu;
   a.w = (const bf16*)w1;
   a.out0 = (bf16*)part;
-  return bn_rows(c.H) == 256 ? row_bm<DX, 256>(c, a, c.H) : row_bm<DX, 128>(c, a, c.H);
+  switch (bn_rows_bf16(c.H, c.BM)) {
+    case 512: return row_bm<DX, 512>(c, a, c.H);
+    case 256: return row_bm<DX, 256>(c, a, c.H);
+  }
+  return row_bm<DX, 128>(c, a, c.H);
 }
 
 template <class Tl>

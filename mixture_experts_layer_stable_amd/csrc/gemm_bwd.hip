@@ -6,12 +6,12 @@
 //   registers). The epilogue fuses the SwiGLU backward and the gate gradient
 //   (router-weight gradients fused into the SwiGLU backward, SonicMoE-style:
 //   dothoosh.com MoK page, "Technical details of the MoK mechanism"):
-//     g'_partial(row, n-tile) = sum over the tile's columns of dA * h
+//     g'_partial(row, 32-column block) = sum over the block's columns of dA * h
 //     dh = g * dA;  da = dh*u*sig(a)*(1 + a*(1 - sig(a)));  du = dh*silu(a)
 //   Partials are summed in a fixed order -- 16 columns sequentially per lane,
-//   the two halves of each 32-column block, blocks in ascending column order,
-//   then N-tiles ascending in the router-backward kernel -- independent of the
-//   wave layout; no float atomics.
+//   the two halves of each 32-column block, then the blocks in ascending column
+//   order in the router-backward kernel -- independent of the tile shape, the
+//   wave layout and the grid; no float atomics.
 // dX: push reverse-dispatch -- q = dGU . W1[e] written to the (token, slot)
 //   partial row perm[row]; reduced per token in slot order afterwards.
 // dW2[e] = sum_r (g*dY)_r^T h_r and dW1[e] = sum_r dGU_r^T x_r: K runs over the
@@ -59,7 +59,6 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs<T> a) {
   __shared__ __align__(16) char smem[Tl::LDS_BYTES];
   __shared__ int s_ts[kMaxEb + 1];
   __shared__ int s_slot[Tl::BM];
-  __shared__ float s_red[Tl::BN / 32][Tl::BM];
   constexpr int BKE = kRowBytes / (int)sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
@@ -105,16 +104,10 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs<T> a) {
       // the 32-column block's sum: columns 0-15 (even lane) + columns 16-31 (odd lane)
       const float other = __shfl_xor(part, 1);
       const float blk = (lane & 1) ? other + part : part + other;
-      if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+      // one partial per 32-column block of I: the sum over blocks (router_bwd, ascending)
+      // does not depend on the tile shape, the wave layout or the grid
+      if ((lane & 1) == 0 && row < t.nrows) a.dgp[(int64_t)((t.n * Tl::BN + col) >> 5) * a.R + t.row0 + row] = blk;
     });
-    // blocks in ascending column order: the result depends on BN only, not on the wave layout
-    __syncthreads();  // s_red from every wave
-    for (int i = tid; i < t.nrows; i += kThreads) {
-      float s = 0.0f;
-#pragma unroll
-      for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
-      a.dgp[(int64_t)t.n * a.R + t.row0 + i] = s;
-    }
   });
 }
 

@@ -164,7 +164,6 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
   __shared__ __align__(1024) char smem[kMxStages * STG];
   __shared__ int s_ts[kMaxEx + 1];
   __shared__ int s_slot[Tl::BM];
-  __shared__ float s_red[KIND == MDH ? Tl::BN / 32 : 1][KIND == MDH ? Tl::BM : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
@@ -276,15 +275,11 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
         }
         const float other = __shfl_xor(part, 1);
         const float blk = (lane & 1) ? other + part : part + other;
-        if ((lane & 1) == 0) s_red[col >> 5][row] = blk;
+        // one partial per 32-column block of I: the sum over blocks (router_bwd, ascending)
+        // does not depend on the tile shape, the wave layout or the grid
+        if ((lane & 1) == 0 && row < t.nrows)
+          a.dgp[(int64_t)((t.n * Tl::BN + col) >> 5) * a.R + t.row0 + row] = blk;
       });
-      __syncthreads();  // s_red from every wave
-      for (int i = tid; i < t.nrows; i += Tl::NT) {
-        float s = 0.0f;
-#pragma unroll
-        for (int b = 0; b < Tl::BN / 32; ++b) s += s_red[b][i];
-        a.dgp[(int64_t)t.n * a.R + t.row0 + i] = s;
-      }
     }
   });
 }

@@ -15,6 +15,7 @@ struct Ctx {
   int max_tiles;
   int num_cu;
   int grid;        // persistent GEMM grid
+  int gemm;        // expert-GEMM dtype (mok_dtype)
   hipStream_t s;
   // schedule table (device)
   int32_t* counts;
@@ -83,7 +84,10 @@ hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const
 // Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
 inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }
 inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }
-// number of N-tiles of the dH GEMM (d-gate partials per routed row)
-inline int dh_ntiles(int I) { return I / bn_rows(I); }
+// bf16 dh/dx GEMMs: 512-wide tiles (8 waves side by side) for 128-row tiles when N allows
+inline int bn_rows_bf16(int N, int BM) { return (BM == 128 && N % 512 == 0) ? 512 : bn_rows(N); }
+// d-gate partials per routed row: one per 32-column block of I (summed in ascending
+// block order by router_bwd, so the bits do not depend on the GEMM's tiling)
+inline int dgate_parts(int I) { return I / 32; }
 
 }  // namespace mok
