@@ -194,3 +194,48 @@ def test_mx_empty_batch_writes_zero_weight_gradients():
     torch.cuda.synchronize()
     for t in (buf.dw1, buf.dw2, buf.dwr):
         assert torch.all(t == 0)
+
+
+def _mx_parity(w, tile_m=0):
+    x, dy, wr, b, w1, w2 = _case(w)
+    g = _run_whole(w, x, dy, wr, b, w1, w2, tile_m=tile_m)
+    idx, gate, f, bw = _oracle(w, x, dy, wr, b, w1, w2)
+    np.testing.assert_array_equal(g["idx"], idx)
+    errs = {
+        "y": rel_fro(np64(g["y"]), f["y"]),
+        "dx": rel_fro(np64(g["dx"]), bw["dx"]),
+        "dgate": rel_fro(g["dgate"].numpy(), bw["dgate"]),
+        "dw1": rel_fro(np64(g["dw1"]), np.stack([bw["dw1"][e] for e in range(w.E)])),
+        "dw2": rel_fro(np64(g["dw2"]), np.stack([bw["dw2"][e] for e in range(w.E)])),
+        "dwr": rel_fro(np64(g["dwr"]), bw["dwr"]),
+    }
+    print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_MX, (k, v)
+
+
+@pytest.mark.parametrize("tile_m", [0, 32])
+def test_mx_ragged_odd_shape(tile_m):
+    """T = 300 tokens, k = 3 of E = 5 experts: segments that are not multiples of 32, 64 or
+    128 rows, a token-block tail in every expert's weight-gradient operands."""
+    w = inputs.replace(MX_CASES["small"], T=300, H=256, E=5, k=3, I=128)
+    print("case T=300 E=5 k=3 tile_m", tile_m, flush=True)
+    _mx_parity(w, tile_m)
+
+
+def test_mx_single_expert_top1():
+    """E = 1, k = 1: every token in one segment, gates exactly 1."""
+    w = inputs.replace(MX_CASES["small"], T=200, H=256, E=1, k=1, I=256)
+    _mx_parity(w)
+
+
+def test_mx_streamed_three_slots_odd_count():
+    """3 micro-batches through a 3-slot ring against one call over the whole batch."""
+    w = inputs.replace(MX_CASES["imbalanced"], T=768)
+    x, dy, wr, b, w1, w2 = _case(w)
+    whole = _run_whole(w, x, dy, wr, b, w1, w2)
+    st = _run_streamed(w, 3, 3, x, dy, wr, b, w1, w2)
+    for n in ("y", "dx", "dgate", "dw1", "dw2", "dwr"):
+        a, c = st[n], whole[n]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           c.view(torch.int16) if c.dtype == torch.bfloat16 else c), n
