@@ -7,21 +7,17 @@
 // internal order). Independent chains are interleaved across registers and
 // lanes; no single chain is reordered.
 //
-// Two workgroup layouts, both with every chain a sequential fp32 FMA over h:
-//  * large batches (route_lds_kernel): 256 threads, TT = 4*TPT tokens x all E
-//    experts; lane l of wave w owns tokens w*TPT.. and experts l + 64*q; 16-h chunks
-//    of x and Wr are staged in LDS as fp32, so each bf16 value is unpacked once per
-//    workgroup; after the H loop every wave holds complete logit rows for its tokens.
-//  * small batches (route_kernel): 64*EPT threads, thread e owns expert e (its Wr row
-//    streams through registers) for TT = 8..32 tokens whose x rows are wave-uniform
-//    (scalar loads feeding the FMA's scalar operand), so a 2048-token batch still
-//    spreads over every compute unit; logits go through LDS once before selection.
-// Selection: k rounds of a wave arg-max with butterfly shuffles.
+// Workgroup: 64*EPT threads, thread e owns expert e for TT = 8, 16 or 32 tokens, so
+// even a 2048-token micro-batch spreads over every compute unit. Each thread streams
+// its Wr row through registers one 64-h chunk ahead of use (cover for L2 latency);
+// 64-h chunks of the TT x rows are unpacked to fp32 in LDS once per workgroup
+// (double-buffered) and read by every lane at the same address (a broadcast). Every
+// logit is a sequential fp32 FMA chain over h. Logits go through LDS once; then
+// selection: k rounds of a wave arg-max with butterfly shuffles.
 #include "kernels.h"
 
 namespace mok {
 
-constexpr int kRouteHC = 16;  // h values per LDS chunk (LDS layout)
 constexpr int kNoExpert = 0x7FFFFFFF;
 
 // Strict total order of candidates: larger value first; equal values
@@ -34,123 +30,6 @@ __device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
   return a > b || (a == b && ea < eb);
 }
 
-template <typename T, int TPT, int EPT>
-__global__ __launch_bounds__(256) void route_lds_kernel(const T* __restrict__ x, const T* __restrict__ wr,
-                                                    const float* __restrict__ bias, int32_t* __restrict__ idx,
-                                                    float* __restrict__ gate, float* __restrict__ logits, int64_t Tn,
-                                                    int H, int E, int k) {
-  constexpr int TT = 4 * TPT;
-  constexpr int EC = 64 * EPT;
-  constexpr int VE = Elem<T>::VE;
-  constexpr int VPR = kRouteHC / VE;  // 16-byte vectors per row chunk
-  __shared__ float sx[TT][kRouteHC];
-  __shared__ float sw[kRouteHC][EC];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * TT;
-
-  float acc[TPT][EPT];
-#pragma unroll
-  for (int i = 0; i < TPT; ++i)
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) acc[i][q] = 0.0f;
-
-  for (int h0 = 0; h0 < H; h0 += kRouteHC) {
-    for (int i = tid; i < TT * VPR; i += 256) {
-      const int t = i / VPR, vv = i % VPR;
-      const int64_t tok = t0 + t;
-      float f[VE];
-      if (tok < Tn) {
-        unpack(ldg16(x + tok * H + h0 + vv * VE), f, (T*)nullptr);
-      } else {
-#pragma unroll
-        for (int q = 0; q < VE; ++q) f[q] = 0.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < VE; ++q) sx[t][vv * VE + q] = f[q];
-    }
-    for (int i = tid; i < EC * VPR; i += 256) {
-      const int e = i / VPR, vv = i % VPR;
-      float f[VE];
-      if (e < E) {
-        unpack(ldg16(wr + (int64_t)e * H + h0 + vv * VE), f, (T*)nullptr);
-      } else {
-#pragma unroll
-        for (int q = 0; q < VE; ++q) f[q] = 0.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < VE; ++q) sw[vv * VE + q][e] = f[q];
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int hh = 0; hh < kRouteHC; ++hh) {
-      float xv[TPT], wv[EPT];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) xv[i] = sx[wave * TPT + i][hh];
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) wv[q] = sw[hh][lane + 64 * q];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i)
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) acc[i][q] = __builtin_fmaf(xv[i], wv[q], acc[i][q]);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int64_t tok = t0 + wave * TPT + i;
-    if (tok < Tn) {  // uniform across the wave
-      float v[EPT];
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const int e = lane + 64 * q;
-        v[q] = acc[i][q];
-        if (bias != nullptr && e < E) v[q] = v[q] + bias[e];
-        if (logits != nullptr && e < E) logits[tok * E + e] = v[q];
-      }
-      // k rounds of wave arg-max; lane j keeps slot j's expert and exp(z_j - z_0)
-      uint32_t taken = 0;
-      float z0 = 0.0f, s = 0.0f, my_ex = 0.0f;
-      int my_e = 0;
-#pragma unroll 1
-      for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int be = kNoExpert;
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) {
-          const int e = lane + 64 * q;
-          if (e < E && !((taken >> q) & 1u) && better(v[q], e, bv, be)) {
-            bv = v[q];
-            be = e;
-          }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const float ov = __shfl_xor(bv, off);
-          const int oe = __shfl_xor(be, off);
-          if (better(ov, oe, bv, be)) {
-            bv = ov;
-            be = oe;
-          }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (j == 0) z0 = bv;
-        const float ex = expf(bv - z0);  // softmax over the selected logits, summed in slot order
-        s = s + ex;
-        if (lane == j) {
-          my_e = be;
-          my_ex = ex;
-        }
-      }
-      if (lane < k) {
-        idx[tok * k + lane] = my_e;
-        gate[tok * k + lane] = my_ex / s;
-      }
-    }
-  }
-}
-
 template <typename T, int TT, int EPT>
 __global__ __launch_bounds__(1024) void route_kernel(const T* __restrict__ x, const T* __restrict__ wr,
                                                      const float* __restrict__ bias, int32_t* __restrict__ idx,
@@ -158,29 +37,65 @@ __global__ __launch_bounds__(1024) void route_kernel(const T* __restrict__ x, co
                                                      int64_t Tn, int H, int E, int k) {
   constexpr int VE = Elem<T>::VE;
   constexpr int EC = 64 * EPT;
+  constexpr int HC = 64;  // h per LDS chunk
+  __shared__ __align__(16) float sx[2][TT][HC];
   __shared__ float sz[TT][EC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int nt = (int)min<int64_t>(TT, Tn - t0);
   const int e = tid;
   const T* wrow = wr + (int64_t)(e < E ? e : 0) * H;
-  // rows past the end re-read the last token; their results are dropped
-  const T* xr = x + min(t0, Tn - 1) * (int64_t)H;
-  const int nt = (int)min<int64_t>(TT, Tn - t0);
 
+  // x chunk -> fp32 in LDS, unpacked once per workgroup (rows past the end re-read the
+  // last token; their results are dropped)
+  const auto stage = [&](int h0, int buf) {
+    for (int i = tid; i < TT * (HC / VE); i += EC) {
+      const int t = i / (HC / VE), v = i % (HC / VE);
+      const int64_t tok = t0 + (t < nt ? t : nt - 1);
+      float f[VE];
+      unpack(ldg16(x + tok * H + h0 + v * VE), f, (T*)nullptr);
+#pragma unroll
+      for (int q = 0; q < VE; q += 4)
+        *reinterpret_cast<float4*>(&sx[buf][t][v * VE + q]) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+    }
+  };
   float acc[TT];
 #pragma unroll
   for (int i = 0; i < TT; ++i) acc[i] = 0.0f;
-#pragma unroll 2
-  for (int h0 = 0; h0 < H; h0 += VE) {
-    float w[VE];
-    unpack(ldg16(wrow + h0), w, (T*)nullptr);
+  const int nc = H / HC;
+  constexpr int NV = HC / VE;  // 16-byte Wr vectors per chunk
+  // this thread's Wr chunk in registers, loaded one chunk ahead (L2 latency cover)
+  uint4 wv[NV], wn[NV];
 #pragma unroll
-    for (int i = 0; i < TT; ++i) {
-      float xv[VE];
-      unpack(ldg16(xr + (int64_t)(i < nt ? i : 0) * H + h0), xv, (T*)nullptr);
+  for (int v = 0; v < NV; ++v) wv[v] = ldg16(wrow + v * VE);
+  stage(0, 0);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nc) {
+      stage((c + 1) * HC, buf ^ 1);
 #pragma unroll
-      for (int j = 0; j < VE; ++j) acc[i] = __builtin_fmaf(xv[j], w[j], acc[i]);
+      for (int v = 0; v < NV; ++v) wn[v] = ldg16(wrow + (c + 1) * HC + v * VE);
     }
+#pragma unroll
+    for (int hv = 0; hv < HC; hv += VE) {
+      float w[VE];
+      unpack(wv[hv / VE], w, (T*)nullptr);
+#pragma unroll
+      for (int i = 0; i < TT; ++i) {
+#pragma unroll
+        for (int q = 0; q < VE; q += 4) {
+          const float4 xv = *reinterpret_cast<const float4*>(&sx[buf][i][hv + q]);  // same address in every lane
+          acc[i] = __builtin_fmaf(xv.x, w[q], acc[i]);
+          acc[i] = __builtin_fmaf(xv.y, w[q + 1], acc[i]);
+          acc[i] = __builtin_fmaf(xv.z, w[q + 2], acc[i]);
+          acc[i] = __builtin_fmaf(xv.w, w[q + 3], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) wv[v] = wn[v];
+    __syncthreads();
   }
   const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
 #pragma unroll
@@ -246,26 +161,17 @@ static hipError_t launch_route_t(const Ctx& c, const void* x, const void* wr, co
   return hipGetLastError();
 }
 
-template <typename T, int TPT, int EPT>
-static hipError_t launch_route_lds(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx,
-                                   float* gate, float* logits) {
-  const int64_t blocks = (c.T + 4 * TPT - 1) / (4 * TPT);
-  hipLaunchKernelGGL((route_lds_kernel<T, TPT, EPT>), dim3((unsigned)blocks), dim3(256), 0, c.s, (const T*)x,
-                     (const T*)wr, bias, idx, gate, logits, c.T, c.H, c.E, c.k);
-  return hipGetLastError();
-}
-
-// Layout choice: the LDS layout once 32-token workgroups give at least two per
-// compute unit; otherwise the register layout with the largest of 32/16/8 tokens
-// per workgroup that still gives two per compute unit (each reads all of Wr).
+// Tokens per workgroup: the largest of 32/16/8 that still gives at least two
+// workgroups per compute unit (each workgroup streams all of Wr once).
 template <typename T, int EPT>
 static hipError_t route_tt(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
                            float* logits) {
   int cus = 256;
   int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  constexpr int TPT = EPT <= 8 ? 8 : 4;
-  if (c.T >= 4LL * TPT * 2 * cus) return launch_route_lds<T, TPT, EPT>(c, x, wr, bias, idx, gate, logits);
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    cus = 256;
+  if (c.T >= 32LL * 2 * cus) return launch_route_t<T, 32, EPT>(c, x, wr, bias, idx, gate, logits);
   if (c.T >= 16LL * 2 * cus) return launch_route_t<T, 16, EPT>(c, x, wr, bias, idx, gate, logits);
   return launch_route_t<T, 8, EPT>(c, x, wr, bias, idx, gate, logits);
 }
