@@ -132,7 +132,7 @@ struct MxLayout {
   size_t xq, xs, hq, hs, part, fslot, fwd;
   size_t dyq, dys, dguq, dgus, bpart, dgp, bslot;
   size_t st_counts, st_offsets, st_perm, st_dz, st_xs, st_dos, st_h, st_dgu;
-  size_t gcnt, pofs, rowmap, xt, xts, dot, dots, ht, hts, dgut, dguts, bwd;
+  size_t gcnt, pofs, rowmap, xt, xts, dot, dots, ht, hts, dgut, dguts, dwrp, bwd;
   int64_t kmax;
 };
 
@@ -178,6 +178,7 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.hts = o; o = up(o + (size_t)(I * K / 32));
   L.dgut = o; o = up(o + (size_t)(2 * I * K));
   L.dguts = o; o = up(o + (size_t)(2 * I * K / 32));
+  L.dwrp = o; o = up(o + dwr_stash_part_bytes((int)E, (int)H));
   L.bwd = o;
   return L;
 }
@@ -337,7 +338,7 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
                                       (int)H, K));
   if (dwr != nullptr)
     MOK_LAUNCH("dwr", c.s, launch_dwr_stash(c, (const float*)(wb + X.st_dz), (const int32_t*)(wb + X.st_perm),
-                                            wb + X.st_xs, gcnt, pofs, rowmap, dwr));
+                                            wb + X.st_xs, gcnt, pofs, rowmap, (float*)(wb + X.dwrp), dwr));
   return MOK_OK;
 }
 

@@ -1,7 +1,8 @@
 // Bandwidth-bound kernels of the layer step, all with fixed summation orders.
 //
 //  combine     y_t = sum_{j=0..k-1} g_tj * partial[t*k+j]            (push combine)
-//  router_bwd  g'_tj = sum over the 32-column blocks of I (ascending) of the d-gate partials;
+//  router_bwd  g'_s = sum over the 32-column blocks of I (ascending) of the d-gate partials
+//              (one thread per routed row), then per token
 //              dz_tj = g_tj * (g'_tj - sum_i g_ti g'_ti)   (softmax over the top k)
 //  dx_reduce   dx_t = sum_j q[t*k+j] + sum_j dz_tj * wr[idx_tj]  (push reverse-dispatch)
 //  dwr         dWr[e] = sum over e's routed rows (ascending slot) of dz_s * x_t
@@ -34,26 +35,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ part
   stg16(y + t * H + h0, pack(acc, (T*)nullptr));
 }
 
-__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgp, const float* __restrict__ gate,
-                                                         const int32_t* __restrict__ inv, float* __restrict__ dgate,
-                                                         float* __restrict__ dz, int64_t T_, int k, int R, int ntn) {
+// g'_s for the slot of routed row r: the d-gate partials of r's 32-column blocks of I,
+// summed in ascending block order (threads of a wave read consecutive rows: coalesced).
+__global__ __launch_bounds__(256) void router_gsum_kernel(const float* __restrict__ dgp,
+                                                          const int32_t* __restrict__ perm,
+                                                          float* __restrict__ dgate, int R, int nb) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  float v = 0.0f;
+  for (int n = 0; n < nb; ++n) v += dgp[(int64_t)n * R + r];
+  dgate[perm[r]] = v;
+}
+
+// dz_tj = g_tj * (g'_tj - sum_i g_ti g'_ti), the sum in slot order.
+__global__ __launch_bounds__(256) void router_dz_kernel(const float* __restrict__ dgate, const float* __restrict__ gate,
+                                                        float* __restrict__ dz, int64_t T_, int k) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T_) return;
-  float gp[16], g[16];
   float s = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t slot = t * k + j;
-    const int r = inv[slot];
-    float v = 0.0f;
-    for (int n = 0; n < ntn; ++n) v += dgp[(int64_t)n * R + r];
-    gp[j] = v;
-    g[j] = gate[slot];
-    s = __builtin_fmaf(g[j], v, s);
-  }
-  for (int j = 0; j < k; ++j) {
-    dgate[t * k + j] = gp[j];
-    dz[t * k + j] = g[j] * (gp[j] - s);
-  }
+  for (int j = 0; j < k; ++j) s = __builtin_fmaf(gate[t * k + j], dgate[t * k + j], s);
+  for (int j = 0; j < k; ++j) dz[t * k + j] = gate[t * k + j] * (dgate[t * k + j] - s);
 }
 
 template <typename T>
@@ -162,8 +163,10 @@ hipError_t launch_combine(const Ctx& c, const void* part, const float* gate, voi
 
 hipError_t launch_router_bwd(const Ctx& c, const float* dgp, const float* gate, float* dgate, float* dz) {
   if (c.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(c.T)), dim3(256), 0, c.s, dgp, gate, c.inv, dgate, dz, c.T,
-                     c.k, c.R, dgate_parts(c.I));
+  hipLaunchKernelGGL(router_gsum_kernel, dim3(blocks_for(c.R)), dim3(256), 0, c.s, dgp, c.perm, dgate, c.R,
+                     dgate_parts(c.I));
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(router_dz_kernel, dim3(blocks_for(c.T)), dim3(256), 0, c.s, dgate, gate, dz, c.T, c.k);
   return hipGetLastError();
 }
 

@@ -68,7 +68,8 @@ hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, 
 hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int32_t* offsets, int M, int32_t* gcnt,
                                  int32_t* pofs, int64_t kmax, int32_t* rowmap);
 hipError_t launch_dwr_stash(const Ctx& c, const float* dz, const int32_t* perm, const void* xs, const int32_t* gcnt,
-                            const int32_t* pofs, const int32_t* rowmap, void* dwr);
+                            const int32_t* pofs, const int32_t* rowmap, float* part, void* dwr);
+size_t dwr_stash_part_bytes(int E, int H);  // fp32 chunk partials of launch_dwr_stash
 // MXFP8 grouped GEMMs
 hipError_t launch_fc1_mx(const Ctx& c, const void* xq, const void* xs, const void* w1q, const void* w1s, void* au,
                          void* h, void* hq, void* hs);

@@ -11,8 +11,9 @@
 //               zero rows, i.e. all-zero blocks, which add nothing).
 //  rowmap       padded segment row -> stash row (micro-batch m's routed row r is stash
 //               row m*R + r); -1 for padding.
-//  dwr_stash    dWr[e] = sum over e's rows of the step, in micro-batch then slot order,
-//               of dz_s * x_t (fp32 fused multiply-adds in that order).
+//  dwr_stash    dWr[e] = sum over e's rows of the step (micro-batch then slot order) of
+//               dz_s * x_t: 8 fixed chunks of consecutive rows summed row by row, then the
+//               chunk sums in ascending order.
 #include "gemm.h"
 #include "kernels.h"
 #include "mx.h"
@@ -173,23 +174,32 @@ hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int3
 
 // dz and perm are [M][R] (micro-batch m's slot-indexed dz and its schedule perm);
 // xs is [M*R][H] (micro-batch m's x rows in routed order at rows m*R ..).
-template <typename TO>
-__global__ __launch_bounds__(256) void dwr_stash_kernel(const float* __restrict__ dz, const int32_t* __restrict__ perm,
-                                                        const bf16* __restrict__ xs, const int32_t* __restrict__ gcnt,
-                                                        const int32_t* __restrict__ pofs,
-                                                        const int32_t* __restrict__ rowmap, TO* __restrict__ dwr,
-                                                        int E, int H, int R) {
+// dWr[e] = sum over kDwrChunks consecutive chunks of e's rows (chunk c = rows
+// [c*n/kDwrChunks, (c+1)*n/kDwrChunks) in step order), each summed row by row with fp32
+// fused multiply-adds, the chunk sums added in ascending order: a hot expert's rows are
+// spread over kDwrChunks threads per column.
+constexpr int kDwrChunks = 8;
+
+__global__ __launch_bounds__(256) void dwr_stash_part_kernel(const float* __restrict__ dz,
+                                                             const int32_t* __restrict__ perm,
+                                                             const bf16* __restrict__ xs,
+                                                             const int32_t* __restrict__ gcnt,
+                                                             const int32_t* __restrict__ pofs,
+                                                             const int32_t* __restrict__ rowmap,
+                                                             float* __restrict__ part, int E, int H, int R) {
   const int vpr = H / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)E * vpr) return;
-  const int e = (int)(gid / vpr);
-  const int h0 = (int)(gid - (int64_t)e * vpr) * 8;
+  if (gid >= (int64_t)E * kDwrChunks * vpr) return;
+  const int h0 = (int)(gid % vpr) * 8;
+  const int64_t ec = gid / vpr;
+  const int c = (int)(ec % kDwrChunks), e = (int)(ec / kDwrChunks);
+  const int n = gcnt[e];
+  const int j0 = (int)((int64_t)c * n / kDwrChunks), j1 = (int)((int64_t)(c + 1) * n / kDwrChunks);
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  const int n = gcnt[e];
   const int32_t* rm = rowmap + pofs[e];
-  for (int j = 0; j < n; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const int row = rm[j];
     const int m = row / R;
     const float d = dz[(int64_t)m * R + perm[row]];
@@ -198,21 +208,37 @@ __global__ __launch_bounds__(256) void dwr_stash_kernel(const float* __restrict_
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
   }
-  TO* o = dwr + (int64_t)e * H + h0;
+  float* o = part + ((int64_t)e * kDwrChunks + c) * H + h0;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void dwr_stash_sum_kernel(const float* __restrict__ part, TO* __restrict__ dwr,
+                                                            int E, int H) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)E * H) return;
+  const int64_t e = gid / H, h = gid % H;
+  float s = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) Elem<TO>::put(o, q, acc[q]);
+  for (int c = 0; c < kDwrChunks; ++c) s += part[(e * kDwrChunks + c) * H + h];
+  Elem<TO>::put(dwr, gid, s);
 }
 
 hipError_t launch_dwr_stash(const Ctx& c, const float* dz, const int32_t* perm, const void* xs, const int32_t* gcnt,
-                            const int32_t* pofs, const int32_t* rowmap, void* dwr) {
-  const int64_t n = (int64_t)c.E * (c.H / 8);
+                            const int32_t* pofs, const int32_t* rowmap, float* part, void* dwr) {
+  const int64_t n = (int64_t)c.E * kDwrChunks * (c.H / 8);
+  hipLaunchKernelGGL(dwr_stash_part_kernel, dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt, pofs,
+                     rowmap, part, c.E, c.H, c.R);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const int64_t m = (int64_t)c.E * c.H;
   if (c.wgrad_f32)
-    hipLaunchKernelGGL((dwr_stash_kernel<float>), dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt,
-                       pofs, rowmap, (float*)dwr, c.E, c.H, c.R);
+    hipLaunchKernelGGL((dwr_stash_sum_kernel<float>), dim3(nblk(m)), dim3(256), 0, c.s, part, (float*)dwr, c.E, c.H);
   else
-    hipLaunchKernelGGL((dwr_stash_kernel<bf16>), dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt,
-                       pofs, rowmap, (bf16*)dwr, c.E, c.H, c.R);
+    hipLaunchKernelGGL((dwr_stash_sum_kernel<bf16>), dim3(nblk(m)), dim3(256), 0, c.s, part, (bf16*)dwr, c.E, c.H);
   return hipGetLastError();
 }
+
+size_t dwr_stash_part_bytes(int E, int H) { return (size_t)E * kDwrChunks * H * sizeof(float); }
 
 }  // namespace mok
