@@ -112,11 +112,12 @@ __device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const S
     const int ahead = KT - 1 - kt;
     wait_tiles_behind<STAGES, NI>(ahead < STAGES - 2 ? ahead : STAGES - 2);
     ring_barrier();
+    // refill with K-tile nk in two bursts, as in the bf16 core: A rows and both
+    // scale rows now, the B rows between the two 64-k steps
     const int nk = kt + STAGES - 1;
+    char* st = smem + (nk % STAGES) * STG;
     if (nk < KT) {
-      char* st = smem + (nk % STAGES) * STG;
       oa.issue(nk, st, wave);
-      ob.issue(nk, st + OFF_B, wave);
       sa.issue(nk, st + OFF_SA, wave);
       sb.issue(nk, st + OFF_SB, wave);
     }
@@ -127,6 +128,7 @@ __device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const S
 #pragma unroll
     for (int fn = 0; fn < Tl::FN; ++fn) xb[fn] = sb.get(cur + OFF_SB, fn, lane);
     mx_kstep<0, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    if (nk < KT) ob.issue(nk, st + OFF_B, wave);
     mx_kstep<1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
   }
   __syncthreads();
