@@ -117,11 +117,14 @@ typedef struct mok_desc {
 
 /* MXFP8 expert weights, quantised once per weight update by mok_weights_quantize.
  * Each orientation is K-contiguous for the GEMM that reads it; *q are E4M3 bytes,
- * *s the E8M0 scale bytes of consecutive 32-element blocks along K.
- *   w1q  [E][2I][H],  w1s  [E][2I][H/32]   fc1 (K = H)
- *   w2q  [E][H][I],   w2s  [E][H][I/32]    fc2 (K = I)
- *   w2tq [E][I][H],   w2ts [E][I][H/32]    dh  (W2 transposed, K = H)
- *   w1tq [E][H][2I],  w1ts [E][H][2I/32]   dx  (W1 transposed, K = 2I) */
+ * *s the E8M0 scale bytes of consecutive 32-element blocks along K, stored
+ * K-tile-major: for every 128-element K-tile, the 4 scale bytes of each row, rows
+ * consecutive, so a GEMM tile's scales for one K-tile are one contiguous run.
+ *   w1q  [E][2I][H],  w1s  [E][H/128][2I][4]    fc1 (K = H)
+ *   w2q  [E][H][I],   w2s  [E][I/128][H][4]     fc2 (K = I)
+ *   w2tq [E][I][H],   w2ts [E][H/128][I][4]     dh  (W2 transposed, K = H)
+ *   w1tq [E][H][2I],  w1ts [E][2I/128][H][4]    dx  (W1 transposed, K = 2I)
+ * (row r's scale of K-block b is byte [b/4][r][b%4] of its expert's array). */
 typedef struct mok_mx_weights {
   void *w1q, *w1s, *w2q, *w2s, *w2tq, *w2ts, *w1tq, *w1ts;
 } mok_mx_weights;

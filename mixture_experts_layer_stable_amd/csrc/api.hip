@@ -535,8 +535,8 @@ mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w
   c.I = d->I;
   c.s = (hipStream_t)stream;
   const int64_t E = d->E, H = d->H, I = d->I;
-  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w1, E * 2 * I, (int)H, out->w1q, out->w1s));
-  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w2, E * H, (int)I, out->w2q, out->w2s));
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w1, E * 2 * I, (int)H, out->w1q, out->w1s, 2 * I));
+  MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w2, E * H, (int)I, out->w2q, out->w2s, H));
   MOK_LAUNCH("quant", c.s, launch_mx_quant_cols(c, w2, H * I, I, nullptr, nullptr, (int)H, (int)I, (int)E, H,
                                                 out->w2tq, out->w2ts));
   MOK_LAUNCH("quant", c.s, launch_mx_quant_cols(c, w1, 2 * I * H, H, nullptr, nullptr, (int)(2 * I), (int)H, (int)E,
@@ -575,6 +575,6 @@ const char* mok_status_string(mok_status s) {
   return "unknown status";
 }
 
-int32_t mok_version(void) { return 200; }
+int32_t mok_version(void) { return 201; }
 
 }  // extern "C"

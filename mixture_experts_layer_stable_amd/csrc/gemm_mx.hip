@@ -36,7 +36,10 @@ __device__ __forceinline__ void dma4_sv(const char* sbase, uint32_t voff, char* 
 
 // Scale dwords of ROWS tile rows per K-tile. Wave w loads rows [w*RPW, (w+1)*RPW)
 // with lanes 0..RPW-1 (one DMA instruction per wave per stage, RPW >= 8 so the
-// instruction always has active lanes).
+// instruction always has active lanes). K-tile kt's dwords sit kt * kstride bytes
+// after K-tile 0's: 4 for row-major scales; the matrix's rows * 4 for K-tile-major
+// ones, whose dwords for consecutive rows are contiguous (one 128-byte request per
+// 32 rows instead of one per row).
 template <int ROWS, int NF, int NW>
 struct OpScale {
   static constexpr int RPW = ROWS / NW;
@@ -44,20 +47,23 @@ struct OpScale {
   static constexpr int BYTES = ROWS * 4;
   const char* sbase;
   uint32_t voff;
+  uint32_t kstride;
   uint32_t foff[NF];
   bool active;
 
-  // rowoff(row) -> byte offset of the row's first scale byte from sbase_ (< 2 GiB)
+  // rowoff(row) -> byte offset of the row's K-tile-0 scale dword from sbase_ (< 2 GiB)
   template <class F, class G>
-  __device__ __forceinline__ void init(const void* sbase_, F rowoff, G frow, int wave, int lane) {
+  __device__ __forceinline__ void init(const void* sbase_, F rowoff, G frow, int wave, int lane,
+                                       uint32_t kstride_ = 4) {
     sbase = reinterpret_cast<const char*>(sbase_);
+    kstride = kstride_;
     active = lane < RPW;
     voff = rowoff(wave * RPW + (active ? lane : 0));
 #pragma unroll
     for (int f = 0; f < NF; ++f) foff[f] = 4u * (uint32_t)(frow(f) + (lane & 31));
   }
   __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
-    const char* b = uniform_ptr(sbase + (int64_t)kt * 4);
+    const char* b = uniform_ptr(sbase + (int64_t)kt * kstride);
     if (active) dma4_sv(b, voff, stage + wave * RPW * 4);
   }
   __device__ __forceinline__ uint32_t get(const char* stage, int f, int lane) const {
@@ -205,13 +211,14 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
       };
       ob.init(a.wq + (int64_t)t.e * I2 * a.H, [&](int j) -> uint32_t { return wrow(j) * (uint32_t)K; }, frow_b, wave,
               lane);
-      sb.init(a.ws + (int64_t)t.e * I2 * KB, [&](int j) -> uint32_t { return wrow(j) * (uint32_t)KB; }, frow_b, wave,
-              lane);
+      sb.init(a.ws + (int64_t)t.e * I2 * KB, [&](int j) -> uint32_t { return wrow(j) * 4u; }, frow_b, wave, lane,
+              (uint32_t)I2 * 4u);
     } else {
       // weight rows n*BN + j of expert e's [N][K] matrix
       const int64_t r0 = (int64_t)t.e * N + (int64_t)t.n * Tl::BN;
       ob.init(a.wq + r0 * K, [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)K; }, frow_b, wave, lane);
-      sb.init(a.ws + r0 * KB, [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)KB; }, frow_b, wave, lane);
+      sb.init(a.ws + (int64_t)t.e * N * KB + (int64_t)t.n * Tl::BN * 4, [&](int j) -> uint32_t { return (uint32_t)j * 4u; },
+              frow_b, wave, lane, (uint32_t)N * 4u);
     }
     f32x16_t acc[Tl::FM][Tl::FN];
     main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, K / 128, smem, wave, lane, acc);
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
 }
 
 // Weight gradients: out[e] [M][N] = sum over k in e's padded segment of A[m][k] B[n][k],
-// A [M][kld] and B [N][kld] E4M3 with scales [M][kld/32], [N][kld/32]; e's segment is
+// A [M][kld] and B [N][kld] E4M3 with K-tile-major scales [kld/128][M][4], [kld/128][N][4]; e's segment is
 // columns pofs[e] .. pofs[e+1] (a multiple of 128; empty -> zeros written).
 struct MxDwArgs {
   const int32_t* pofs;
@@ -313,7 +320,6 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
   const int mt = rem / NT, nt = rem - mt * NT;
   const int64_t k0 = a.pofs[e];
   const int KT = (int)((a.pofs[e + 1] - k0) / 128);
-  const int64_t kb = a.kld / 32;
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
   const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
   OA oa;
@@ -322,12 +328,12 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
   SB sb;
   oa.init(a.aq + (int64_t)mt * Tl::BM * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
           frow_a, wave, lane);
-  sa.init(a.as + (int64_t)mt * Tl::BM * kb + k0 / 32, [&](int r) -> uint32_t { return (uint32_t)(r * kb); }, frow_a,
-          wave, lane);
+  sa.init(a.as + (k0 / 128) * a.M * 4 + (int64_t)mt * Tl::BM * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
+          frow_a, wave, lane, (uint32_t)a.M * 4u);
   ob.init(a.bq + (int64_t)nt * Tl::BN * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
           frow_b, wave, lane);
-  sb.init(a.bs + (int64_t)nt * Tl::BN * kb + k0 / 32, [&](int r) -> uint32_t { return (uint32_t)(r * kb); }, frow_b,
-          wave, lane);
+  sb.init(a.bs + (k0 / 128) * a.N * 4 + (int64_t)nt * Tl::BN * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
+          frow_b, wave, lane, (uint32_t)a.N * 4u);
   f32x16_t acc[Tl::FM][Tl::FN];
   main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
   TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;

@@ -57,9 +57,11 @@ hipError_t launch_dw1_bf16(const Ctx& c, const void* dgu, const void* xs, void* 
 hipError_t launch_gather_rows(const Ctx& c, const void* src, const float* gate, void* dst);
 
 // MXFP8: quantisers (E4M3 elements + E8M0 scale bytes per 32 along K)
-// rows x F bf16 -> q [rows][F], s [rows][F/32] (blocks along each row)
-hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s);
-// transposed, blocks along rows: q [mats][F][out_ld], s [mats][F][out_ld/32]; logical
+// rows x F bf16 -> q [rows][F] and scales of the 32-blocks along each row: s [rows][F/32]
+// when kmaj_rows = 0, else per matrix of kmaj_rows rows K-tile-major [F/128][kmaj_rows][4]
+hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s,
+                                int64_t kmaj_rows = 0);
+// transposed, blocks along rows: q [mats][F][out_ld], s K-tile-major [mats][out_ld/128][F][4]; logical
 // row r of matrix z reads physical row rowmap[r] (or r) of src + z*src_mat (ld elements
 // per row); K logical rows (multiple of 128), row blocks at or past *kdev skipped
 hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, int64_t ld, const int32_t* rowmap,

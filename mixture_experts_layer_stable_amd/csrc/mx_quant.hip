@@ -24,8 +24,12 @@ static unsigned nblk(int64_t n, int b = 256) { return (unsigned)((n + b - 1) / b
 
 // nvec = (rows * F) / 16 sixteen-element vectors; F % 32 == 0, so vector pairs
 // (2j, 2j+1) are exactly the 32-element blocks and block b's scale is s[b].
+// Scale byte of block b (32 features) of row r: row-major (kmaj_rows = 0) at
+// r * F/32 + b; K-tile-major (kmaj_rows > 0 = rows per matrix) at
+// [z][b/4][r % kmaj_rows][b % 4] with z = r / kmaj_rows.
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restrict__ src, int64_t nvec,
-                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s, int F,
+                                                            int64_t kmaj_rows) {
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= nvec) return;  // nvec and blockDim are even: a pair leaves together
   float f[16];
@@ -33,21 +37,31 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restri
   uint32_t sb;
   const uint4 o = mx_quant16_pair(f, &sb);
   stg16(q + v * 16, o);
-  if ((v & 1) == 0) s[v >> 1] = (uint8_t)sb;
+  if ((v & 1) == 0) {
+    int64_t i = v >> 1;
+    if (kmaj_rows > 0) {
+      const int64_t nb = F / 32, row = i / nb, b = i - row * nb, z = row / kmaj_rows, r = row - z * kmaj_rows;
+      i = z * kmaj_rows * nb + (b >> 2) * kmaj_rows * 4 + r * 4 + (b & 3);
+    }
+    s[i] = (uint8_t)sb;
+  }
 }
 
-hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s) {
+hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int F, void* q, void* s,
+                                int64_t kmaj_rows) {
   const int64_t nvec = rows * (F / 16);
   if (nvec == 0) return hipSuccess;
   hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(nblk(nvec)), dim3(256), 0, c.s, (const bf16*)src, nvec, (uint8_t*)q,
-                     (uint8_t*)s);
+                     (uint8_t*)s, F, kmaj_rows);
   return hipGetLastError();
 }
 
 // Transposing quantiser. Matrix z = blockIdx.z; logical row r in [0, K) reads
 // physical row rowmap[r] (rowmap != nullptr; < 0 = zero row) or r of
 // src + z * src_mat, ld elements per physical row; feature f in [0, F).
-// Writes q[(z*F + f) * out_ld + r] and s[(z*F + f) * (out_ld/32) + r/32].
+// Writes q[(z*F + f) * out_ld + r] and the scale of block b = r/32 K-tile-major,
+// s[z*F*(out_ld/32) + (b/4)*F*4 + f*4 + b%4]: each 128-row K-tile's scale dwords of
+// consecutive features are contiguous.
 // Workgroup: 128 logical rows x 64 features; wave w quantises block w (32 rows)
 // of the 64 features. Row blocks at or past *kdev (when given) are skipped.
 struct ColQuantArgs {
@@ -99,7 +113,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
   uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;
   stg16(qo, make_uint4(w[0], w[1], w[2], w[3]));
   stg16(qo + 16, make_uint4(w[4], w[5], w[6], w[7]));
-  a.s[orow * (a.out_ld / 32) + r0 / 32 + b] = (uint8_t)sb;
+  const int64_t kb = r0 / 32 + b;
+  a.s[(int64_t)z * a.F * (a.out_ld / 32) + (kb >> 2) * a.F * 4 + (int64_t)(f0 + f) * 4 + (kb & 3)] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, int64_t ld, const int32_t* rowmap,

@@ -191,10 +191,11 @@ class MxWeights:
     def __init__(self, d: Desc, device="cuda"):
         E, H, I = d.E, d.H, d.I
         u8 = dict(dtype=torch.uint8, device=device)
-        self.w1q, self.w1s = torch.empty(E, 2 * I, H, **u8), torch.empty(E, 2 * I, H // 32, **u8)
-        self.w2q, self.w2s = torch.empty(E, H, I, **u8), torch.empty(E, H, I // 32, **u8)
-        self.w2tq, self.w2ts = torch.empty(E, I, H, **u8), torch.empty(E, I, H // 32, **u8)
-        self.w1tq, self.w1ts = torch.empty(E, H, 2 * I, **u8), torch.empty(E, H, 2 * I // 32, **u8)
+        # scales K-tile-major: [E][K/128][rows][4]
+        self.w1q, self.w1s = torch.empty(E, 2 * I, H, **u8), torch.empty(E, H // 128, 2 * I, 4, **u8)
+        self.w2q, self.w2s = torch.empty(E, H, I, **u8), torch.empty(E, I // 128, H, 4, **u8)
+        self.w2tq, self.w2ts = torch.empty(E, I, H, **u8), torch.empty(E, H // 128, I, 4, **u8)
+        self.w1tq, self.w1ts = torch.empty(E, H, 2 * I, **u8), torch.empty(E, 2 * I // 128, H, 4, **u8)
 
     def c(self) -> _MxWeights:
         return _MxWeights(*[getattr(self, n).data_ptr() for n in MX_FIELDS])

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(mok):
     for n in _declared():
         assert hasattr(lib, n), n
     assert set(_declared()) == set(mok.EXPORTS)
-    assert mok.version() == 200
+    assert mok.version() == 201
 
 
 def test_status_strings(mok):

@@ -63,7 +63,9 @@ def test_weights_quantize_bit_exact():
     }
     for name, (tq, ts, ref, ax) in cases.items():
         el, s = orc.mx.mx_quantize(ref, ax)
-        got_s = ts.cpu().numpy().astype(np.int64) - 127
+        # stored K-tile-major [E][K/128][rows][4] -> [E][rows][K/32]
+        kt = ts.cpu().numpy().astype(np.int64)
+        got_s = np.ascontiguousarray(kt.transpose(0, 2, 1, 3)).reshape(s.shape) - 127
         np.testing.assert_array_equal(got_s, s, err_msg=name + " scales")
         np.testing.assert_array_equal(_decode_e4m3(tq), el, err_msg=name + " elements")
 
