@@ -349,27 +349,37 @@ __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, ch
   __syncthreads();
 }
 
-// bf16 epilogue through a per-wave patch of 32 rows x 40 bf16 (2560 bytes, outside
-// the ring): lane (row = lane/2, half = lane&1) stores 16 consecutive bf16 of a row of
-// each 32x32 block as two 16-byte vectors: FM*FN*2 global stores per lane.
+// bf16 epilogue through a per-wave LDS patch: each pair of horizontally adjacent
+// 32x32 accumulator blocks (fn, fn+1) is converted into a 32-row x 64-column bf16
+// patch (row pitch 72 elements), then read back so that every store instruction
+// writes 8 whole rows of 128 contiguous bytes (lane: row = 8i + lane/8, 16-byte
+// chunk lane%8). FM*FN*2 global stores per lane, as store(row, col, v) with v the
+// 8 bf16 at tile (row, col .. col+7). The patch (kBf16PatchBytes) lies outside any
+// ring stage still in use; a wave's LDS operations run in issue order.
+constexpr int kBf16PatchBytes = 32 * 72 * 2;
+
 template <class Tl, class F>
 __device__ __forceinline__ void epilogue_bf16(f32x16_t (&acc)[Tl::FM][Tl::FN], char* patch, int wm, int wn, int lane,
                                               F&& store) {
-  constexpr int PLD = 40;
+  static_assert(Tl::FN % 2 == 0, "blocks are stored in horizontal pairs");
+  constexpr int PLD = 72;
   uint16_t* p = reinterpret_cast<uint16_t*>(patch);
 #pragma unroll
   for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < Tl::FN; ++fn) {
+    for (int fn = 0; fn < Tl::FN; fn += 2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         p[row * PLD + (lane & 31)] = (uint16_t)f32_to_bf16(acc[fm][fn][r]);
+        p[row * PLD + 32 + (lane & 31)] = (uint16_t)f32_to_bf16(acc[fm][fn + 1][r]);
       }
-      const int row = lane >> 1, c0 = (lane & 1) * 16;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(patch + (row * PLD + c0) * 2);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(patch + (row * PLD + c0 + 8) * 2);
-      store(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c0, v0, v1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + (lane >> 3), c = (lane & 7) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(patch + (row * PLD + c) * 2);
+        store(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c, v);
+      }
     }
 }
 

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   using OB = OpMN<Tl::BN, 32, Tl::FN, Tl::NW>;
   constexpr int STAGES = 3;
   constexpr int SB = OA::BYTES + OB::BYTES;
-  constexpr int PATCH = 32 * 40 * 2;
+  constexpr int PATCH = kBf16PatchBytes;
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
   __shared__ __align__(1024) char smem[STAGES * SB + Tl::NW * PATCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -254,11 +254,8 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
       setup(Ln);
       ring_prologue<STAGES>(oa, ob, KT, smem, wave);
     }
-    epilogue_bf16<Tl>(acc, patch, wm, wn, lane, [&](int row, int col, const uint4& v0, const uint4& v1) {
-      bf16* p = out + (int64_t)row * a.N + col;
-      stg16(p, v0);
-      stg16(p + 8, v1);
-    });
+    epilogue_bf16<Tl>(acc, patch, wm, wn, lane,
+                      [&](int row, int col, const uint4& v) { stg16(out + (int64_t)row * a.N + col, v); });
     if (Ln >= hi) break;
     L = Ln;
     first = false;
