@@ -97,13 +97,15 @@ __device__ __forceinline__ void mx_kstep(const OA& oa, const OB& ob, const char*
 }
 
 // STAGES-deep ring as in the bf16 core; a stage holds A rows, B rows, A scales, B scales.
-template <class Tl, int STAGES, class OA, class OB, class SA, class SB>
-__device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
-                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+// Split like the bf16 core's ring_prologue / ring_loop: the prologue issues the first
+// STAGES-1 K-tiles; the loop's waits for those K-tiles may leave EXTRA younger global
+// stores per lane outstanding (a persistent kernel's previous epilogue), while any later
+// K-tile, issued after those stores, covers them (vector memory completes in order).
+template <int STAGES, class OA, class OB, class SA, class SB>
+__device__ __forceinline__ void mx_ring_prologue(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
+                                                 char* smem, int wave) {
   constexpr int OFF_B = OA::BYTES, OFF_SA = OA::BYTES + OB::BYTES, OFF_SB = OFF_SA + SA::BYTES;
   constexpr int STG = OFF_SB + SB::BYTES;
-  constexpr int NI = OA::NI + OB::NI + 2;
-  zero_acc<Tl>(acc);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
     if (s < KT) {
@@ -114,9 +116,19 @@ __device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const S
       sb.issue(s, st + OFF_SB, wave);
     }
   }
+}
+
+template <class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB>
+__device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
+                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  static_assert(STAGES == 3, "the waits are written for 3 stages");
+  constexpr int OFF_B = OA::BYTES, OFF_SA = OA::BYTES + OB::BYTES, OFF_SB = OFF_SA + SA::BYTES;
+  constexpr int STG = OFF_SB + SB::BYTES;
+  constexpr int NI = OA::NI + OB::NI + 2;
+  zero_acc<Tl>(acc);
   for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = KT - 1 - kt;
-    wait_tiles_behind<STAGES, NI>(ahead < STAGES - 2 ? ahead : STAGES - 2);
+    const bool pro = kt < STAGES - 1;  // issued by mx_ring_prologue, before any EXTRA stores
+    if (kt + 1 < KT) wait_vmcnt_extra<NI, EXTRA>(pro); else wait_vmcnt_extra<0, EXTRA>(pro);
     ring_barrier();
     // refill with K-tile nk in two bursts, as in the bf16 core: A rows and both
     // scale rows now, the B rows between the two 64-k steps
@@ -138,6 +150,13 @@ __device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const S
     mx_kstep<1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
   }
   __syncthreads();
+}
+
+template <class Tl, int STAGES, class OA, class OB, class SA, class SB>
+__device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
+                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
+  mx_ring_loop<Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
 }
 
 template <int BM, int BN>
@@ -342,6 +361,80 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
   });
 }
 
+// Persistent form of dw_mx_kernel for bf16 gradients (the same tiles and arithmetic):
+// a workgroup walks tiles L = lo + li, lo + li + nx, ... of its XCD's contiguous part
+// of the (expert, M-tile, N-tile) range; the next tile's first K-tiles are issued
+// before this tile's epilogue, whose stores then drain under the next K-loop. The
+// epilogue's per-wave patches use the ring stage that this prologue leaves free.
+template <class Tl>
+__global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
+  using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
+  using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  constexpr int STAGES = kMxStages;
+  constexpr int STG = OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES;
+  constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
+  static_assert(Tl::NW * kBf16PatchBytes <= STG, "epilogue patches fit in one ring stage");
+  __shared__ __align__(1024) char smem[STAGES * STG];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
+  char* patch = smem + (STAGES - 1) * STG + wave * kBf16PatchBytes;
+  const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  const int64_t total = (int64_t)E * MT * NT;
+  const int P = min(8, (int)gridDim.x);
+  const int xcd = blockIdx.x % P;
+  const int nx = ((int)gridDim.x - xcd + P - 1) / P;
+  const int li = blockIdx.x / P;
+  const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
+  int64_t L = lo + li;
+  if (L >= hi) return;
+  const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
+  const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
+  OA oa;
+  OB ob;
+  SA sa;
+  SB sb;
+  int e = 0, mt = 0, nt = 0, KT = 0;
+  const auto setup = [&](int64_t l) {
+    e = __builtin_amdgcn_readfirstlane((int)(l / (MT * NT)));
+    const int rem = (int)(l - (int64_t)e * MT * NT);
+    mt = __builtin_amdgcn_readfirstlane(rem / NT);
+    nt = __builtin_amdgcn_readfirstlane(rem - mt * NT);
+    const int64_t k0 = __builtin_amdgcn_readfirstlane(a.pofs[e]);
+    KT = __builtin_amdgcn_readfirstlane((int)((a.pofs[e + 1] - k0) / 128));
+    oa.init(a.aq + (int64_t)mt * Tl::BM * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+            frow_a, wave, lane);
+    sa.init(a.as + (k0 / 128) * a.M * 4 + (int64_t)mt * Tl::BM * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
+            frow_a, wave, lane, (uint32_t)a.M * 4u);
+    ob.init(a.bq + (int64_t)nt * Tl::BN * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+            frow_b, wave, lane);
+    sb.init(a.bs + (k0 / 128) * a.N * 4 + (int64_t)nt * Tl::BN * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
+            frow_b, wave, lane, (uint32_t)a.N * 4u);
+  };
+  setup(L);
+  mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
+  bool first = true;
+  for (;;) {
+    f32x16_t acc[Tl::FM][Tl::FN];
+    if (first)
+      mx_ring_loop<Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+    else
+      mx_ring_loop<Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+    bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
+    const int64_t Ln = L + nx;
+    if (Ln < hi) {
+      setup(Ln);
+      mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
+    }
+    epilogue_bf16<Tl>(acc, patch, wm, wn, lane,
+                      [&](int row, int col, const uint4& v) { stg16(out + (int64_t)row * a.N + col, v); });
+    if (Ln >= hi) break;
+    L = Ln;
+    first = false;
+  }
+}
+
 // ---------------------------------------------------------------------------
 static Sched sched_of_mx(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
 
@@ -432,6 +525,11 @@ template <class Tl>
 static hipError_t dw_launch_mx(const Ctx& c, const MxDwArgs& a) {
   const int64_t blocks = (int64_t)c.E * (a.M / Tl::BM) * (a.N / Tl::BN);
   if (blocks == 0) return hipSuccess;
+  if (!c.wgrad_f32) {
+    const int g = (int)std::min<int64_t>(c.grid > 0 ? c.grid : c.num_cu, blocks);
+    hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    return hipGetLastError();
+  }
   if (c.wgrad_f32)
     hipLaunchKernelGGL((dw_mx_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
   else
