@@ -7,8 +7,8 @@
 // internal order). Independent chains are interleaved across registers and
 // lanes; no single chain is reordered.
 //
-// Workgroup: 64*EPT threads, thread e owns expert e for TT = 8, 16 or 32 tokens, so
-// even a 2048-token micro-batch spreads over every compute unit. Each thread streams
+// Workgroup: 64*EPT threads, thread e owns expert e for TT = 4, 8, 16 or 32 tokens, so
+// even a 2048-token micro-batch spreads over every compute unit (two workgroups each). Each thread streams
 // its Wr row through registers one 64-h chunk ahead of use (cover for L2 latency);
 // 64-h chunks of the TT x rows are unpacked to fp32 in LDS once per workgroup
 // (double-buffered) and read by every lane at the same address (a broadcast). Every
@@ -161,8 +161,9 @@ static hipError_t launch_route_t(const Ctx& c, const void* x, const void* wr, co
   return hipGetLastError();
 }
 
-// Tokens per workgroup: the largest of 32/16/8 that still gives at least two
-// workgroups per compute unit (each workgroup streams all of Wr once).
+// Tokens per workgroup: the largest of 32/16/8/4 that still gives at least two
+// workgroups per compute unit (each workgroup streams all of Wr once; at 2048 tokens
+// 4 beats 8 by a fifth, 2 loses to 4).
 template <typename T, int EPT>
 static hipError_t route_tt(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
                            float* logits) {
@@ -173,7 +174,8 @@ static hipError_t route_tt(const Ctx& c, const void* x, const void* wr, const fl
     cus = 256;
   if (c.T >= 32LL * 2 * cus) return launch_route_t<T, 32, EPT>(c, x, wr, bias, idx, gate, logits);
   if (c.T >= 16LL * 2 * cus) return launch_route_t<T, 16, EPT>(c, x, wr, bias, idx, gate, logits);
-  return launch_route_t<T, 8, EPT>(c, x, wr, bias, idx, gate, logits);
+  if (c.T >= 8LL * 2 * cus) return launch_route_t<T, 8, EPT>(c, x, wr, bias, idx, gate, logits);
+  return launch_route_t<T, 4, EPT>(c, x, wr, bias, idx, gate, logits);
 }
 
 template <typename T>

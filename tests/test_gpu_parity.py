@@ -89,6 +89,29 @@ def test_tiny_fp32_backward_parity():
     _full(w)
 
 
+@pytest.mark.parametrize("T", [3000, 5000, 9000, 17000])
+def test_route_token_group_sizes(T):
+    """The router picks 4, 8, 16 or 32 tokens per workgroup by batch size (3000, 5000, 9000
+    and 17000 tokens select each of them on 256 compute units; the last group is ragged):
+    logits and indices equal the oracle's bit for bit, gates within 1e-6."""
+    import oracle as orc
+    from mixture_experts_layer_stable_amd import mok
+
+    w = _w("imbalanced_bf16", T=T, E=72, k=3, H=256, I=128)
+    print("case T=%d E=%d k=%d H=%d" % (w.T, w.E, w.k, w.H), flush=True)
+    x, wr, b = inputs.make_x(w), inputs.make_wr(w), inputs.make_bias(w)
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16)
+    idx = torch.empty(w.T, w.k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(w.T, w.k, dtype=torch.float32, device="cuda")
+    logits = torch.empty(w.T, w.E, dtype=torch.float32, device="cuda")
+    mok.route(d, x.cuda(), wr.cuda(), None if b is None else b.cuda(), idx, gate, logits)
+    torch.cuda.synchronize()
+    z, oi, og = orc.route(x.float().numpy(), wr.float().numpy(), w.k, None if b is None else b.numpy())
+    np.testing.assert_array_equal(logits.cpu().numpy(), z)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    assert rel_fro(gate.cpu().double().numpy(), og) <= 1e-6
+
+
 @pytest.mark.parametrize("T,E,k,H,I", [(77, 5, 2, 128, 128), (130, 100, 3, 256, 384), (40, 600, 4, 128, 128),
                                        (33, 8, 8, 128, 256), (50, 1, 1, 128, 128)])
 def test_ragged_and_odd_shapes(T, E, k, H, I):
