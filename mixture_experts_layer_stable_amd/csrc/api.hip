@@ -296,7 +296,7 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
   char* st_dgu = wb + X.st_dgu + (size_t)(m * R * 2 * I * 2);
   if (c.R > 0) {
     float* dgp = (float*)(bs + X.dgp);
-    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, dy, c.T, c.H, bs + X.dyq, bs + X.dys));
+    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, dy, c.T, c.H, bs + X.dyq, bs + X.dys, c.T));
     MOK_LAUNCH("dh", c.s, launch_dh_mx(c, bs + X.dyq, bs + X.dys, q->w2tq, q->w2ts, sv + L.au, sv + L.h, gate, st_dgu,
                                        bs + X.dguq, bs + X.dgus, dgp));
     MOK_LAUNCH("router_bwd", c.s, launch_router_bwd(c, dgp, gate, dgate, dz));
@@ -448,7 +448,7 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
     MOK_REQUIRE(q->w2s);
     const MxLayout X = mx_layout_of(d);
     char* fs = (char*)ws + (size_t)(d->mb_index % ring_of(d)) * X.fslot;
-    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, x, c.T, c.H, fs + X.xq, fs + X.xs));
+    MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, x, c.T, c.H, fs + X.xq, fs + X.xs, c.T));
     MOK_LAUNCH("fc1", c.s, launch_fc1_mx(c, fs + X.xq, fs + X.xs, q->w1q, q->w1s, sv + L.au, sv + L.h, fs + X.hq,
                                          fs + X.hs));
     MOK_LAUNCH("fc2", c.s, launch_fc2_mx(c, fs + X.hq, fs + X.hs, q->w2q, q->w2s, fs + X.part));

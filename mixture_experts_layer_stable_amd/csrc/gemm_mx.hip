@@ -176,7 +176,7 @@ struct MxRowArgs {
   const bf16* h;      // dh
   const float* gate;  // dh
   float* dgp;         // dh
-  int H, I, k, R;
+  int H, I, k, R, T;  // T = tokens of the micro-batch (R = T * k)
 };
 
 enum MxKind { MFC1 = 0, MFC2 = 1, MDH = 2, MDX = 3 };
@@ -210,13 +210,13 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
       // pull dispatch / reverse-combine: token rows gathered through perm (padding rows re-read row 0)
       const auto tok = [&](int row) { return (uint32_t)(s_slot[row < t.nrows ? row : 0] / a.k); };
       oa.init(a.aq, [&](int row) -> uint32_t { return tok(row) * (uint32_t)K; }, frow_a, wave, lane);
-      sa.init(a.as, [&](int row) -> uint32_t { return tok(row) * (uint32_t)KB; }, frow_a, wave, lane);
+      sa.init(a.as, [&](int row) -> uint32_t { return tok(row) * 4u; }, frow_a, wave, lane, (uint32_t)a.T * 4u);
     } else {
       const auto rr = [&](int row) { return (uint32_t)(row < t.nrows ? row : 0); };
       oa.init(a.aq + (int64_t)t.row0 * K, [&](int row) -> uint32_t { return rr(row) * (uint32_t)K; }, frow_a, wave,
               lane);
-      sa.init(a.as + (int64_t)t.row0 * KB, [&](int row) -> uint32_t { return rr(row) * (uint32_t)KB; }, frow_a,
-              wave, lane);
+      sa.init(a.as + (int64_t)t.row0 * 4, [&](int row) -> uint32_t { return rr(row) * 4u; }, frow_a, wave, lane,
+              (uint32_t)a.R * 4u);
     }
     OB ob;
     SB sb;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
         uint32_t sbyte;
         const uint4 q = mx_quant16_pair(hv, &sbyte);
         stg16(a.oq + R * a.I + c, q);
-        if ((lane & 1) == 0) a.os[R * (a.I / 32) + (c >> 5)] = (uint8_t)sbyte;
+        if ((lane & 1) == 0) a.os[(int64_t)(c >> 7) * a.R * 4 + R * 4 + ((c >> 5) & 3)] = (uint8_t)sbyte;
       });
     } else if constexpr (KIND == MFC2 || KIND == MDX) {
       epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane,
@@ -297,8 +297,9 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
           stg16(a.oq + R * I2 + c, q1);
           stg16(a.oq + R * I2 + a.I + c, q2);
           if ((lane & 1) == 0) {
-            a.os[R * (I2 / 32) + (c >> 5)] = (uint8_t)s1;
-            a.os[R * (I2 / 32) + ((a.I + c) >> 5)] = (uint8_t)s2;
+            const int c2 = a.I + c;
+            a.os[(int64_t)(c >> 7) * a.R * 4 + R * 4 + ((c >> 5) & 3)] = (uint8_t)s1;
+            a.os[(int64_t)(c2 >> 7) * a.R * 4 + R * 4 + ((c2 >> 5) & 3)] = (uint8_t)s2;
           }
         }
         const float other = __shfl_xor(part, 1);
@@ -465,6 +466,7 @@ static MxRowArgs mx_args(const Ctx& c) {
   a.I = c.I;
   a.k = c.k;
   a.R = c.R;
+  a.T = (int)c.T;
   return a;
 }
 
