@@ -6,7 +6,8 @@
   step, which quantises every GEMM operand at the same points: rel. Frobenius <= 2e-2;
 * the streamed step (micro-batches through the ring, weight gradients deferred to the
   last backward call) bit-identical to one call over the whole batch;
-* repeated steps bit-identical; an empty batch still writes zero weight gradients.
+* repeated steps, and persistent grids of 1, 7 and 300 workgroups, bit-identical; an
+  empty batch still writes zero weight gradients.
 """
 import numpy as np
 import pytest
@@ -102,9 +103,10 @@ def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True):
     return out
 
 
-def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0):
+def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0):
     mok = _mok()
-    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m, mb_count=M, ring=ring)
+    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m, mb_count=M, ring=ring,
+                 grid=grid)
     st = mok.StreamedStep(d, DEV)
     q = mok.MxWeights(d, DEV)
     mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
@@ -167,6 +169,22 @@ def test_mx_streamed_equals_whole_batch():
         a, c = st[n], whole[n]
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            c.view(torch.int16) if c.dtype == torch.bfloat16 else c), n
+
+
+def test_mx_grids_bit_identical():
+    """Persistent grids of 1, 7 and 300 workgroups (the row GEMMs and the pipelined
+    weight-gradient kernel walk their tiles in a different order and number of passes)
+    give the same bits as the default one-per-CU grid."""
+    w = MX_CASES["imbalanced"]
+    case = _case(w)
+    ref = _run_streamed(w, 4, 2, *case)
+    for grid in (1, 7, 300):
+        print("case imbalanced streamed 4x, grid", grid, flush=True)
+        got = _run_streamed(w, 4, 2, *case, grid=grid)
+        for n in ref:
+            a, b = ref[n], got[n]
+            same = np.array_equal(a, b) if isinstance(a, np.ndarray) else torch.equal(a, b)
+            assert same, ("grid", grid, n)
 
 
 def test_mx_repeat_bit_identical():
