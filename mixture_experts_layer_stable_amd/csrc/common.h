@@ -26,6 +26,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats -> two bf16 packed in one dword (lo in bits 0..15), round to nearest
+// even, by the hardware conversion (v_cvt_pk_bf16_f32). For finite values and
+// infinities it gives the same bits as f32_to_bf16; NaN inputs do not occur here.
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw_t));
+}
+
 // Element traits: storage type T, elements per 16-byte vector, load/store of one element as float.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -56,10 +66,10 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[4], float*) {
 }
 __device__ __forceinline__ uint4 pack(const float (&f)[8], bf16*) {
   uint4 r;
-  r.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
-  r.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
-  r.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
-  r.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
+  r.x = bf16x2_rne(f[0], f[1]);
+  r.y = bf16x2_rne(f[2], f[3]);
+  r.z = bf16x2_rne(f[4], f[5]);
+  r.w = bf16x2_rne(f[6], f[7]);
   return r;
 }
 __device__ __forceinline__ uint4 pack(const float (&f)[4], float*) {

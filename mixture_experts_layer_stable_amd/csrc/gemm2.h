@@ -351,28 +351,40 @@ __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, ch
 
 // bf16 epilogue through a per-wave LDS patch: each pair of horizontally adjacent
 // 32x32 accumulator blocks (fn, fn+1) is converted into a 32-row x 64-column bf16
-// patch (row pitch 72 elements), then read back so that every store instruction
-// writes 8 whole rows of 128 contiguous bytes (lane: row = 8i + lane/8, 16-byte
-// chunk lane%8). FM*FN*2 global stores per lane, as store(row, col, v) with v the
-// 8 bf16 at tile (row, col .. col+7). The patch (kBf16PatchBytes) lies outside any
-// ring stage still in use; a wave's LDS operations run in issue order.
-constexpr int kBf16PatchBytes = 32 * 72 * 2;
+// patch (row pitch 96 elements = 48 dwords, so the two rows one half-wave writes fall
+// on disjoint banks), then read back so that every store instruction writes 8 whole
+// rows of 128 contiguous bytes (lane: row = 8i + lane/8, 16-byte chunk lane%8).
+// Accumulator registers r, r+1 (r even) of a lane hold rows rho, rho+1 of its column;
+// converting them as one packed pair and swapping halves with the neighbouring lane
+// (DPP quad_perm [1,0,3,2] + v_perm_b32) gives the even lane (rho, c..c+1) and the odd
+// lane (rho+1, c-1..c) as whole dwords: three VALU ops and one 4-byte LDS write per
+// two values. FM*FN*2 global stores per lane, as store(row, col, v) with v the 8 bf16
+// at tile (row, col .. col+7). The patch (kBf16PatchBytes) lies outside any ring
+// stage still in use; a wave's LDS operations run in issue order.
+constexpr int kBf16PatchLd = 96;
+constexpr int kBf16PatchBytes = 32 * kBf16PatchLd * 2;
 
 template <class Tl, class F>
 __device__ __forceinline__ void epilogue_bf16(f32x16_t (&acc)[Tl::FM][Tl::FN], char* patch, int wm, int wn, int lane,
                                               F&& store) {
   static_assert(Tl::FN % 2 == 0, "blocks are stored in horizontal pairs");
-  constexpr int PLD = 72;
-  uint16_t* p = reinterpret_cast<uint16_t*>(patch);
+  constexpr int PLD = kBf16PatchLd;
+  const int odd = lane & 1;
+  const uint32_t sel = odd ? 0x07060302u : 0x01000504u;
+  const int cpair = (lane & 31) & ~1;
 #pragma unroll
   for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Tl::FN; fn += 2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        p[row * PLD + (lane & 31)] = (uint16_t)f32_to_bf16(acc[fm][fn][r]);
-        p[row * PLD + 32 + (lane & 31)] = (uint16_t)f32_to_bf16(acc[fm][fn + 1][r]);
+      for (int r = 0; r < 16; r += 2) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + odd;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const uint32_t p = bf16x2_rne(acc[fm][fn + hb][r], acc[fm][fn + hb][r + 1]);
+          const uint32_t q = __builtin_amdgcn_mov_dpp(p, 0xB1, 0xF, 0xF, true);
+          *reinterpret_cast<uint32_t*>(patch + (row * PLD + 32 * hb + cpair) * 2) = __builtin_amdgcn_perm(p, q, sel);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
