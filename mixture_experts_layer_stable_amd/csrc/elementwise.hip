@@ -88,32 +88,52 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(const T* __restrict__ pa
   stg16(dx + t * H + h0, pack(acc, (T*)nullptr));
 }
 
+// dWr[e] = sum over e's routed rows r of dz[perm[r]] * x[token of r]. Workgroup =
+// (expert, block of kDwrVec 16-byte column vectors): thread (row lane l, vector v) sums
+// rows l, l + 32, l + 64, ... of the expert in ascending order; then the 32 row-lane
+// sums of each column are added in ascending lane order. The order depends only on
+// the expert's row count (not on the grid), and a hot expert's rows are spread over
+// 32 threads per column.
+constexpr int kDwrVec = 8, kDwrLanes = 32;
+
 template <typename T, typename TO>
-__global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dz, const T* __restrict__ x,
-                                                  const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ perm, TO* __restrict__ dwr, int E, int H,
-                                                  int k) {
+__global__ __launch_bounds__(kDwrVec * kDwrLanes) void dwr_kernel(const float* __restrict__ dz,
+                                                                  const T* __restrict__ x,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ perm,
+                                                                  TO* __restrict__ dwr, int E, int H, int k) {
   constexpr int VE = Elem<T>::VE;
+  constexpr int COLS = kDwrVec * VE;
+  __shared__ float red[kDwrLanes][COLS + 1];
   const int vpr = H / VE;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)E * vpr) return;
-  const int e = (int)(gid / vpr);
-  const int h0 = (int)(gid - (int64_t)e * vpr) * VE;
+  const int nvb = (vpr + kDwrVec - 1) / kDwrVec;
+  const int e = (int)(blockIdx.x / nvb), vb = (int)(blockIdx.x % nvb);
+  const int tv = threadIdx.x % kDwrVec, rl = threadIdx.x / kDwrVec;
+  const int v = vb * kDwrVec + tv;
   float acc[VE];
 #pragma unroll
   for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
-  const int r1 = offsets[e + 1];
-  for (int r = offsets[e]; r < r1; ++r) {
-    const int s = perm[r];
-    const float d = dz[s];
-    float f[VE];
-    unpack(ldg16(x + (int64_t)(s / k) * H + h0), f, (T*)nullptr);
+  if (v < vpr) {
+    const int r1 = offsets[e + 1];
+    for (int r = offsets[e] + rl; r < r1; r += kDwrLanes) {
+      const int s = perm[r];
+      const float d = dz[s];
+      float f[VE];
+      unpack(ldg16(x + (int64_t)(s / k) * H + v * VE), f, (T*)nullptr);
 #pragma unroll
-    for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+      for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+    }
   }
-  TO* o = dwr + (int64_t)e * H + h0;
 #pragma unroll
-  for (int q = 0; q < VE; ++q) Elem<TO>::put(o, q, acc[q]);
+  for (int q = 0; q < VE; ++q) red[rl][tv * VE + q] = acc[q];
+  __syncthreads();
+  if (threadIdx.x < COLS) {
+    const int col = (int)threadIdx.x;
+    float sum = 0.0f;
+#pragma unroll 8
+    for (int l = 0; l < kDwrLanes; ++l) sum += red[l][col];
+    if (vb * kDwrVec + col / VE < vpr) Elem<TO>::put(dwr + (int64_t)e * H, (int64_t)vb * COLS + col, sum);
+  }
 }
 
 // dst[r] = src[perm[r] / k] (* gate[perm[r]], rounded to bf16): token rows in routed order.
@@ -184,15 +204,19 @@ hipError_t launch_dx_reduce(const Ctx& c, const void* part, const float* dz, con
 }
 
 hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr) {
+  const int ve = c.act == MOK_F32 ? 4 : 8;
+  const int64_t nvb = ((int64_t)(c.H / ve) + kDwrVec - 1) / kDwrVec;
+  const dim3 grid((unsigned)(c.E * nvb)), block(kDwrVec * kDwrLanes);
+  if (c.E * nvb == 0) return hipSuccess;
   if (c.act == MOK_F32) {
-    hipLaunchKernelGGL((dwr_kernel<float, float>), dim3(blocks_for((int64_t)c.E * (c.H / 4))), dim3(256), 0, c.s, dz,
-                       (const float*)x, c.offsets, c.perm, (float*)dwr, c.E, c.H, c.k);
+    hipLaunchKernelGGL((dwr_kernel<float, float>), grid, block, 0, c.s, dz, (const float*)x, c.offsets, c.perm,
+                       (float*)dwr, c.E, c.H, c.k);
   } else if (c.wgrad_f32) {
-    hipLaunchKernelGGL((dwr_kernel<bf16, float>), dim3(blocks_for((int64_t)c.E * (c.H / 8))), dim3(256), 0, c.s, dz,
-                       (const bf16*)x, c.offsets, c.perm, (float*)dwr, c.E, c.H, c.k);
+    hipLaunchKernelGGL((dwr_kernel<bf16, float>), grid, block, 0, c.s, dz, (const bf16*)x, c.offsets, c.perm,
+                       (float*)dwr, c.E, c.H, c.k);
   } else {
-    hipLaunchKernelGGL((dwr_kernel<bf16, bf16>), dim3(blocks_for((int64_t)c.E * (c.H / 8))), dim3(256), 0, c.s, dz,
-                       (const bf16*)x, c.offsets, c.perm, (bf16*)dwr, c.E, c.H, c.k);
+    hipLaunchKernelGGL((dwr_kernel<bf16, bf16>), grid, block, 0, c.s, dz, (const bf16*)x, c.offsets, c.perm,
+                       (bf16*)dwr, c.E, c.H, c.k);
   }
   return hipGetLastError();
 }

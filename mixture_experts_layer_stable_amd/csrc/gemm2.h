@@ -204,13 +204,15 @@ struct OpMN {
 #pragma unroll
       for (int j = 0; j < NI; ++j) dma16_sv(b, voff[j], stage + (wave + NW * j) * 1024);
     } else {
+      // tail K-tile: rows past cnt read the zero block at the same column chunk;
+      // addresses derive from the 32-bit offsets (no 64-bit per-lane state kept)
+      const char* b = sbase + (int64_t)k0 * ld;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int o = (wave + NW * j) * 1024 + 16 * (threadIdx.x & 63);
         const int kr = o / PITCH;
-        const uint32_t col = voff[j] - (uint32_t)(kr * ld);
-        const char* p = k0 + kr < cnt ? sbase + (int64_t)(k0 + kr) * ld + col
-                                      : reinterpret_cast<const char*>(g_zero_1k) + col;
+        const char* p = k0 + kr < cnt ? b + voff[j]
+                                      : reinterpret_cast<const char*>(g_zero_1k) + (voff[j] - (uint32_t)(kr * ld));
         dma16(p, stage + (wave + NW * j) * 1024);
       }
     }

@@ -202,6 +202,8 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
 // the ring prologue of the next tile is issued before this tile's epilogue, so the
 // epilogue's stores drain while the next tile's first K-tiles load. The workgroup
 // walks a contiguous range of the tile list (e, mt, nt), one range per XCD.
+// When the per-wave patches fit in one ring stage they use the stage that the next
+// tile's prologue leaves free (stage STAGES-1); otherwise they follow the ring.
 template <class Tl>
 __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E) {
   using OA = OpMN<Tl::BM, 32, Tl::FM, Tl::NW>;
@@ -209,11 +211,12 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   constexpr int STAGES = 3;
   constexpr int SB = OA::BYTES + OB::BYTES;
   constexpr int PATCH = kBf16PatchBytes;
+  constexpr bool IN_RING = Tl::NW * PATCH <= SB;
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
-  __shared__ __align__(1024) char smem[STAGES * SB + Tl::NW * PATCH];
+  __shared__ __align__(1024) char smem[STAGES * SB + (IN_RING ? 0 : Tl::NW * PATCH)];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
-  char* patch = smem + STAGES * SB + wave * PATCH;
+  char* patch = smem + (IN_RING ? (STAGES - 1) * SB : STAGES * SB) + wave * PATCH;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
   const int64_t total = (int64_t)E * MT * NT;
   const int P = min(8, (int)gridDim.x);
