@@ -410,6 +410,8 @@ mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const flo
   c.I = d->I;
   c.act = d->act;
   c.s = (hipStream_t)stream;
+  st = device_cus(&c.num_cu);
+  if (st != MOK_OK) return st;
   MOK_LAUNCH("route", c.s, launch_route(c, x, wr, bias, idx, gate, logits));
   return MOK_OK;
 }

@@ -250,13 +250,6 @@ __device__ __forceinline__ void wait_tiles_behind(int behind) {
 // on the Kimi-K2-shaped layer, this is 2-5% faster than one burst for the row
 // GEMMs; issuing most of the bytes in the first half gains nothing.
 // ---------------------------------------------------------------------------
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 template <class Tl, class OA, class OB>
 __device__ __forceinline__ void ktile_mma(const OA& oa, const OB& ob, const char* cur, bool more, int nk, char* st,
