@@ -62,8 +62,12 @@ hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int
 // Writes q[(z*F + f) * out_ld + r] and the scale of block b = r/32 K-tile-major,
 // s[z*F*(out_ld/32) + (b/4)*F*4 + f*4 + b%4]: each 128-row K-tile's scale dwords of
 // consecutive features are contiguous.
-// Workgroup: 128 logical rows x 64 features; wave w quantises block w (32 rows)
-// of the 64 features. Row blocks at or past *kdev (when given) are skipped.
+// Workgroup: 128 logical rows x 64 features. Wave w quantises features 16w .. 16w+15;
+// lane l takes feature 16w + l/4 and row block l%4, so the 4 lanes of a feature write
+// its 128 consecutive output bytes (and 4 consecutive scale bytes) together. In LDS,
+// row r of the tile is stored rotated by 16 columns when (r / 32) is odd: the 64 lanes
+// of a read then hit every bank exactly twice. Row blocks at or past *kdev (when given)
+// are skipped.
 struct ColQuantArgs {
   const bf16* src;
   int64_t src_mat, ld;
@@ -93,21 +97,23 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) f[q] = 0.0f;
     }
+    const int pc = (c8 + 16 * ((row >> 5) & 1)) & 63;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) tile[row][c8 + q] = f[q];
+    for (int q = 0; q < 8; ++q) tile[row][pc + q] = f[q];
   }
   __syncthreads();
-  const int f = threadIdx.x & 63, b = threadIdx.x >> 6;
+  const int f = 16 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 2), b = threadIdx.x & 3;
+  const int pf = (f + 16 * (b & 1)) & 63;  // rows 32b .. 32b+31 all carry the same rotation
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][f]));
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][pf]));
   const uint32_t sb = mx_scale_byte(m);
   const float inv = mx_inv_scale(sb);
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = 32 * b + 4 * j;
-    w[j] = mx_pack4(tile[i][f], tile[i + 1][f], tile[i + 2][f], tile[i + 3][f], inv);
+    w[j] = mx_pack4(tile[i][pf], tile[i + 1][pf], tile[i + 2][pf], tile[i + 3][pf], inv);
   }
   const int64_t orow = (int64_t)z * a.F + f0 + f;
   uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;

@@ -113,9 +113,12 @@ def test_route_token_group_sizes(T):
 
 
 @pytest.mark.parametrize("T,E,k,H,I", [(77, 5, 2, 128, 128), (130, 100, 3, 256, 384), (40, 600, 4, 128, 128),
-                                       (33, 8, 8, 128, 256), (50, 1, 1, 128, 128)])
+                                       (33, 8, 8, 128, 256), (50, 1, 1, 128, 128), (96, 40, 3, 384, 256),
+                                       (64, 64, 2, 2048, 128)])
 def test_ragged_and_odd_shapes(T, E, k, H, I):
-    """Token counts that are not tile multiples, E not a multiple of 64, E > 512, k = E, E = 1."""
+    """Token counts that are not tile multiples, E not a multiple of 64, E > 512, k = E, E = 1;
+    H = 384 (six 64-h chunks: a partial group of the small-batch router's 4-chunk Wr
+    prefetch) and H = 2048 (the largest H whose x rows that router stages whole)."""
     w = _w("small_bf16", T=T, E=E, k=k, H=H, I=I)
     print("case", w, flush=True)
     _full(w)
