@@ -60,7 +60,10 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
   using OBK = typename std::conditional<K32, OpK32<Tl::BN, Tl::FN, Tl::NW>, OpK<Tl::BN, Tl::FN, Tl::NW>>::type;
   using OB = typename std::conditional<B_MN, OpMN<Tl::BN, OA::BK, Tl::FN, Tl::NW>, OBK>::type;
   constexpr int SB = OA::BYTES + OB::BYTES;
-  __shared__ __align__(1024) char smem[kRowStages * SB];
+  // a fourth ring stage where it fits (32-row tiles: their short per-K-tile work leaves the
+  // DMA latency exposed with only two K-tiles in flight)
+  constexpr int STAGES = 4 * SB + 8 * 1024 <= 160 * 1024 ? 4 : kRowStages;
+  __shared__ __align__(1024) char smem[STAGES * SB];
   __shared__ int s_ts[kMaxE2 + 1];
   __shared__ int s_slot[Tl::BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm2_kernel(RowArgs a) {
               [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)(2 * a.I); }, frow_b, wave, lane);
     }
     f32x16_t acc[Tl::FM][Tl::FN];
-    main_loop2<Tl, kRowStages>(oa, ob, K / OA::BK, smem, wave, wm, wn, lane, acc);
+    main_loop2<Tl, STAGES>(oa, ob, K / OA::BK, smem, wave, wm, wn, lane, acc);
 
     if constexpr (KIND == FC1) {
       const int cbase = t.n * (Tl::BN / 2);

@@ -117,7 +117,77 @@ __global__ __launch_bounds__(64) void sched_rank_kernel(const int32_t* __restric
   }
 }
 
+// Tiny batches (R * E <= 2^14): the three steps in one workgroup of 16 waves, with idx
+// staged in LDS; wave w counts and then ranks experts w, w + 16, ... as the per-expert
+// waves above do (ranks by ascending slot), so every output is the same; two launches
+// fewer. Measured: 64 tokens x 8 experts 11-14 -> 6 us; at 4096 routed rows x 32 experts
+// the one workgroup takes 33 us against 19 us for the three kernels, hence the bound.
+constexpr int kSchedFusedMaxR = 16384;
+
+__global__ __launch_bounds__(1024) void sched_fused_kernel(const int32_t* __restrict__ idx, int R, int E, int BM,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ tile_start,
+                                                           int32_t* __restrict__ num_tiles, int4* __restrict__ tiles,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int s_idx[kSchedFusedMaxR];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_wave[17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < R; i += 1024) s_idx[i] = idx[i];
+  __syncthreads();
+  for (int e = wave; e < E; e += 16) {
+    int cnt = 0;
+    for (int i = lane; i < R; i += 64) cnt += s_idx[i] == e;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) s_cnt[e] = cnt;
+  }
+  __syncthreads();
+  const int e = tid;
+  const int c = e < E ? s_cnt[e] : 0;
+  const int nt = (c + BM - 1) / BM;
+  int tot_c, tot_t;
+  const int off = block_exclusive_scan(c, s_wave, &tot_c);
+  const int ts = block_exclusive_scan(nt, s_wave, &tot_t);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    s_off[e] = off;
+    tile_start[e] = ts;
+    for (int m = 0; m < nt; ++m) tiles[ts + m] = make_int4(e, off + m * BM, min(BM, c - m * BM), 0);
+  }
+  if (e == 0) {
+    offsets[E] = R;
+    tile_start[E] = tot_t;
+    *num_tiles = tot_t;
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int ex = wave; ex < E; ex += 16) {
+    const int base = s_off[ex];
+    int running = 0;
+    for (int i0 = 0; i0 < R; i0 += 64) {
+      const int sl = i0 + lane;
+      const bool m = sl < R && s_idx[sl] == ex;
+      const uint64_t b = __ballot(m);
+      if (m) {
+        const int r = running + __popcll(b & lt);
+        perm[base + r] = sl;
+        inv[sl] = base + r;
+      }
+      running += __popcll(b);
+    }
+  }
+}
+
 hipError_t launch_schedule(const Ctx& c, const int32_t* idx) {
+  if (c.R <= kSchedFusedMaxR && c.E <= 1024 && (int64_t)c.R * c.E <= (int64_t)1 << 14) {
+    hipLaunchKernelGGL(sched_fused_kernel, dim3(1), dim3(1024), 0, c.s, idx, c.R, c.E, c.BM, c.counts, c.offsets,
+                       c.tile_start, c.num_tiles, c.tiles, c.perm, c.inv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(sched_count_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.counts);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, c.s, c.counts, c.E, c.R, c.BM, c.offsets,
                      c.tile_start, c.num_tiles, c.tiles);
