@@ -64,10 +64,11 @@ hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int
 // consecutive features are contiguous.
 // Workgroup: 128 logical rows x 64 features. Wave w quantises features 16w .. 16w+15;
 // lane l takes feature 16w + l/4 and row block l%4, so the 4 lanes of a feature write
-// its 128 consecutive output bytes (and 4 consecutive scale bytes) together. In LDS,
-// row r of the tile is stored rotated by 16 columns when (r / 32) is odd: the 64 lanes
-// of a read then hit every bank exactly twice. Row blocks at or past *kdev (when given)
-// are skipped.
+// its 128 consecutive output bytes (and 4 consecutive scale bytes) together. In LDS (row
+// pitch 65 floats), the rows of row blocks 2 and 3 are stored rotated by 16 columns: the
+// 64 lanes of a column read (16 features x 4 row blocks) then start on 64 different
+// 4-byte banks modulo 256 bytes (and cover each bank of a 128-byte window twice). Row
+// blocks at or past *kdev (when given) are skipped.
 struct ColQuantArgs {
   const bf16* src;
   int64_t src_mat, ld;
@@ -97,13 +98,13 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) f[q] = 0.0f;
     }
-    const int pc = (c8 + 16 * ((row >> 5) & 1)) & 63;
+    const int pc = (c8 + 16 * ((row >> 6) & 1)) & 63;
 #pragma unroll
     for (int q = 0; q < 8; ++q) tile[row][pc + q] = f[q];
   }
   __syncthreads();
   const int f = 16 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 2), b = threadIdx.x & 3;
-  const int pf = (f + 16 * (b & 1)) & 63;  // rows 32b .. 32b+31 all carry the same rotation
+  const int pf = (f + 16 * (b >> 1)) & 63;  // rows 32b .. 32b+31 all carry the same rotation
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][pf]));
