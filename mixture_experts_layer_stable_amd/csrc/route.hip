@@ -32,8 +32,8 @@ __device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
 
 // FULLX (small H, 4-token workgroups): the workgroup's x rows are unpacked into LDS for
 // all of H at once (one load latency instead of one per chunk), each thread keeps its Wr
-// row PD = 4 chunks ahead in registers, there is no barrier inside the h loop, and the 4
-// chains of a lane alternate instruction by instruction. Every chain is the same
+// row PD = 4 (bf16) or 2 (fp32) chunks ahead in registers, there is no barrier inside the
+// h loop, and the 4 chains of a lane alternate instruction by instruction. Every chain is the same
 // sequence of FMAs as in the chunked form. Measured at 2048 tokens, H = 1024, E = 32:
 // 45 -> 37 us with the first three changes.
 constexpr int kRouteFullXMaxH = 2048;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(FULLX ? 64 * EPT : 1024) void route_kernel(const T*
       for (int q = 0; q < VE; q += 4)
         *reinterpret_cast<float4*>(&sxf[t][v * VE + q]) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
     }
-    constexpr int PD = 4;
+    constexpr int PD = sizeof(T) == 2 ? 4 : 2;  // fp32 rows: 2 chunks = 128 registers
     uint4 wb[PD][NV];
 #pragma unroll
     for (int j = 0; j < PD - 1; ++j)
@@ -218,7 +218,7 @@ template <typename T, int TT, int EPT>
 static hipError_t launch_route_t(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx,
                                  float* gate, float* logits) {
   const int64_t blocks = (c.T + TT - 1) / TT;
-  if constexpr (sizeof(T) == 2 && TT == 4 && EPT <= 2) {
+  if constexpr (TT == 4 && EPT <= 2) {
     if (c.H <= kRouteFullXMaxH) {
       hipLaunchKernelGGL((route_kernel<T, TT, EPT, true>), dim3((unsigned)blocks), dim3(64 * EPT), 0, c.s,
                          (const T*)x, (const T*)wr, bias, idx, gate, logits, c.T, c.H, c.E, c.k);
