@@ -18,8 +18,9 @@ Quantisation points of the step (each GEMM operand along that GEMM's K):
   dx   dGU rows (bf16 as stored) along 2I,  W1^T rows along 2I
   dw2  dO = bf16(g*dY) and h along tokens
   dw1  dGU and x along tokens
-For the weight gradients, token blocks start at each expert's first row within each
-micro-batch and the last block of a segment is padded with zeros. The gate gradient is
+For the weight gradients, token blocks start at each expert's first row of the whole
+step (all micro-batches, in token order) and the last block is padded with zeros; the
+`segments` argument of backward_mx restarts blocks at other segment boundaries instead. The gate gradient is
 g' = <dA, h> with dA the dh GEMM result (the fused SonicMoE-style form; with quantised
 operands it is the method's definition).
 """

@@ -200,3 +200,44 @@ def test_storage_rounding_points_bf16():
     for name in ("dgu", "q", "dx", "dwr"):
         v = bwd[name] if name != "dwr" else bwd[name]
         np.testing.assert_array_equal(v, orc.bf16_round(v))
+
+
+def test_storage_points_hand_worked_h_from_unrounded_a_u():
+    """Hand-worked example of where bf16 rounding happens in the forward: h is formed from
+    the fp32 accumulators a and u, and only the stored a, u, h are rounded.
+
+    x = [1, 2^-10], W1 gate row [1, 1], up row [2, 4]: a = 1 + 2^-10, u = 2 + 2^-8 exactly.
+    Stored a, u round to 1 and 2 (both less than half a bf16 step away).
+    h = silu(1 + 2^-10) * (2 + 2^-8) = 1.466788...; in steps of 2^-7 that is 187.749, so
+    the stored h is 188 * 2^-7 = 1.46875 (silu(1) * 2 = 1.462117 = 187.151 steps would
+    give 1.4609375: the mistake of forming h from the rounded a and u)."""
+    x = np.array([[1.0, 2.0 ** -10]])
+    w1 = np.array([[[1.0, 1.0], [2.0, 4.0]]])           # [E=1, 2I=2, H=2]
+    w2 = np.array([[[1.0], [1.0]]])                      # [E=1, H=2, I=1]
+    W = orc.DenseWeights(w1, w2)
+    idx = np.zeros((1, 1), dtype=np.int32)
+    fwd = orc.forward(x, W, idx, np.ones((1, 1)), "bf16", 1, 1)
+    assert fwd["a"][0, 0] == 1.0 and fwd["u"][0, 0] == 2.0
+    assert fwd["h"][0, 0] == 1.46875
+    # o = W2 h from the stored h: both partial columns equal the stored h
+    np.testing.assert_array_equal(fwd["p"][0], [1.46875, 1.46875])
+
+
+def test_storage_points_hand_worked_do_rounded_before_dw2():
+    """Hand-worked example: the dW2 operand dO = g*dY is stored (rounded to bf16) before the
+    weight-gradient GEMM.
+
+    Two tokens routed to the one expert with gate 0.625, H = I = 1, stored h = 1 for both,
+    dY = 1.0234375 and -1. dO = 0.6396484375 (163.75 steps of 2^-8, so 164 * 2^-8 =
+    0.640625 stored) and -0.625 (exact). dW2 = 0.640625 - 0.625 = 2^-6 exactly; with dO
+    left unrounded it would be 0.0146484375 = 15 * 2^-10 (also a bf16 value, so the final
+    rounding of dW2 keeps the two apart)."""
+    T, I = 2, 1
+    x = np.array([[1.0], [1.0]])
+    W = orc.DenseWeights(np.ones((1, 2, 1)), np.ones((1, 1, 1)))
+    idx = np.zeros((T, 1), dtype=np.int32)
+    g = np.full((T, 1), 0.625)
+    fwd = dict(a=np.ones((T, I)), u=np.ones((T, I)), h=np.ones((T, I)), o=np.ones((T, 1)))
+    dy = np.array([[1.0234375], [-1.0]])
+    b = orc.backward(x, W, np.zeros((1, 1)), idx, g, fwd, dy, "bf16", I, router=False)
+    assert b["dw2"][0][0, 0] == 2.0 ** -6

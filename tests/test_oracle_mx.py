@@ -373,3 +373,36 @@ def test_mx_expert_subset_matches_full_step():
     np.testing.assert_array_equal(be["dgate"].ravel()[s], b["dgate"].ravel()[s])
     np.testing.assert_array_equal(be["dw1"][1], b["dw1"][1])
     np.testing.assert_array_equal(be["dw2"][1], b["dw2"][1])
+
+
+def test_mx_storage_points_hand_worked():
+    """Hand-worked MXFP8 example of the storage points.
+
+    Forward: x = [1, 2^-10, 0, ...] (H = 32), W1 gate row [1, 1, 0, ...], up row [2, 4, 0, ...]
+    are exact under MX quantisation (block scales 2^-8 and 2^-6, elements 256, 0.25 and
+    128, 256), so a = 1 + 2^-10 and u = 2 + 2^-8 as in the bf16 example and the stored
+    h is 1.46875, not the 1.4609375 that rounded a and u would give.
+
+    Backward: dO = g*dY is rounded to bf16 before its token-axis MX blocks. Tokens with
+    gate 0.75 and dY = 0.95703125 and -1 give dO = 0.7177734375 = 367.5 * 2^-9 and -0.75.
+    The block scale is 2^-9 (amax 0.75). The bf16 value is 368 * 2^-9, an E4M3 tie between
+    352 and 384 that goes to the even 384, so with stored h = 1 for both tokens dW2 = 0;
+    quantising the unrounded 367.5 would give 352 and dW2 = -32 * 2^-9 = -0.0625."""
+    H, I = 32, 32
+    x = np.zeros((1, H))
+    x[0, :2] = [1.0, 2.0 ** -10]
+    w1 = np.zeros((1, 2 * I, H))
+    w1[0, 0, :2] = [1.0, 1.0]
+    w1[0, I, :2] = [2.0, 4.0]
+    W = orc.DenseWeights(w1, np.ones((1, H, I)))
+    f = mx.forward_mx(x, W, np.zeros((1, 1), np.int32), np.ones((1, 1)), 1, I)
+    assert f["a"][0, 0] == 1.0 and f["u"][0, 0] == 2.0 and f["h"][0, 0] == 1.46875
+
+    T = 2
+    xs = np.ones((T, H))
+    dy = np.zeros((T, H))
+    dy[:, 0] = [0.95703125, -1.0]
+    fwd = dict(a=np.ones((T, I)), u=np.ones((T, I)), h=np.ones((T, I)))
+    b = mx.backward_mx(xs, W, np.zeros((1, H)), np.zeros((T, 1), np.int32), np.full((T, 1), 0.75), fwd, dy, I,
+                        router=False)
+    assert np.all(b["dw2"][0][0] == 0.0)
