@@ -31,6 +31,14 @@ METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; grouped-GEMM MFMA util %"
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 GEMMS = ("fc1", "fc2", "dh", "dx", "dw2", "dw1")
+# Compulsory-work bound of one whole step (ms): the larger of the expert-GEMM flops at the
+# dense MFMA peak and the compulsory HBM bytes (weights once per pass, or once per
+# micro-batch when streamed; activations once) at 8 TB/s. 2048-token bf16 steps: 0.46 GB
+# -> 0.058 ms; Kimi-K2 bf16: 34.6 TFLOP (13.9 ms) against 121 GB (15.1 ms); streamed
+# MXFP8: 328 GB of weight re-reads and activations -> 41 ms. The 64-token fp32 step is
+# bound by launch latency and has none.
+STEP_ROOFLINE_MS = {"small_bf16": 0.058, "imbalanced_bf16": 0.058, "kimi_k2_bf16": 15.1,
+                    "kimi_k2_mxfp8_stream": 41.0}
 
 
 def launch_flops(w, name):
@@ -175,6 +183,18 @@ def cpu_baseline(w, ntok, kept):
     return dt, cores, int(np.asarray(idx).size)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +321,8 @@ def main():
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},
         "gemm_mfma_util_pct": mfma_util,
+        "step_roofline": ({"ms": STEP_ROOFLINE_MS[w.name], "tokens_per_s": w.T / (STEP_ROOFLINE_MS[w.name] * 1e-3),
+                           "frac": STEP_ROOFLINE_MS[w.name] / ms_step} if w.name in STEP_ROOFLINE_MS else None),
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
     }
 
@@ -309,7 +331,7 @@ def main():
         torch.cuda.empty_cache()
         dt, cores, rows = cpu_baseline(w, ntok, kept)
         result["cpu_baseline"] = {
-            "value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": "first %d of %d tokens (%d routed rows): oracle%s route + forward + backward, %.1f s" % (
                 ntok, w.T, rows, " MXFP8" if mx else "", dt)}
     print(json.dumps(result), flush=True)

@@ -46,10 +46,18 @@
  *  - Layouts: x, y, dy, dx [T][H]; wr [E][H]; w1 [E][2I][H] (rows 0..I-1 are
  *    the SwiGLU gate projection, rows I..2I-1 the up projection); w2 [E][H][I];
  *    idx [T][k] int32; gate, dgate, logits [T][k] / [T][E] fp32.
- *  - Errors: arguments are checked before anything is enqueued and a status
- *    is returned; nothing is thrown across the ABI.  A failed launch returns
- *    MOK_ERR_HIP.  Faults inside kernels surface at the caller's next
- *    synchronisation of `stream`.
+ *  - Errors: arguments (pointers, alignment, descriptor, buffer sizes) are
+ *    checked before anything is enqueued and a status is returned; nothing is
+ *    thrown across the ABI.  A failed launch returns MOK_ERR_HIP.  Faults inside
+ *    kernels surface at the caller's next synchronisation of `stream`.
+ *  - Schedule check: mok_schedule_build stamps a header at the start of the
+ *    schedule buffer with a hash of the descriptor it was built for (T, H, E, k,
+ *    I, act, gemm, the resolved tile height and tile capacity).  Every kernel of
+ *    mok_moe_forward / mok_moe_backward compares that hash with the hash of its
+ *    own descriptor first; on a mismatch it writes nothing but the header's
+ *    status word (MOK_ERR_SCHEDULE_MISMATCH) and exits, so a schedule built for
+ *    another problem is never used to index memory.  The caller reads the status
+ *    word (mok_schedule_layout.status) after synchronising the stream.
  *  - Determinism: no floating-point atomics are used; every reduction runs in
  *    a fixed order, so repeated calls with the same inputs and descriptor give
  *    bit-identical outputs.
@@ -70,7 +78,10 @@ typedef enum mok_status {
   MOK_ERR_ALIGN = 2, /* a pointer is not 16-byte aligned */
   MOK_ERR_SHAPE = 3, /* a size in the descriptor is out of range (see mok_desc) */
   MOK_ERR_DTYPE = 4, /* unsupported dtype combination */
-  MOK_ERR_HIP = 5    /* a HIP call (device query or kernel launch) failed */
+  MOK_ERR_HIP = 5,   /* a HIP call (device query or kernel launch) failed */
+  MOK_ERR_WORKSPACE = 6,         /* a caller buffer is smaller than mok_workspace_query asks */
+  MOK_ERR_SCHEDULE_MISMATCH = 7  /* the schedule was built for another descriptor (reported
+                                    in the schedule header's status word, see above) */
 } mok_status;
 
 typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
@@ -153,6 +164,10 @@ typedef struct mok_sizes {
 } mok_sizes;
 
 /* Byte offsets of the schedule table's parts inside the schedule buffer.
+ *   header int32[16] at offset 0: [0] 0x4D4F4B53, [1] descriptor hash, [2] tile
+ *                              height, [3] tile capacity, [4] status (MOK_OK after
+ *                              mok_schedule_build; MOK_ERR_SCHEDULE_MISMATCH once a
+ *                              forward/backward kernel saw another descriptor's hash)
  *   counts[E] int32            rows routed to each expert
  *   offsets[E+1] int32         exclusive prefix sum of counts; offsets[E] = R
  *   tile_start[E+1] int32      first tile of each expert; tile_start[E] = number of tiles
@@ -163,9 +178,12 @@ typedef struct mok_sizes {
  * Rows of one expert are contiguous and in ascending slot order (a stable
  * sort of the slots by expert); tiles list experts in ascending order. */
 typedef struct mok_schedule_layout {
+  size_t status; /* byte offset of the header's status word */
   size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles;
   int32_t tile_m;
   int32_t max_tiles;
+  uint32_t hash; /* descriptor hash stamped into the header */
+  int32_t reserved;
 } mok_schedule_layout;
 
 /* Layout of the `saved` buffer: au [R][2I] (fp32 accumulators a = x.W1_gate,
@@ -175,10 +193,30 @@ typedef struct mok_saved_layout {
   size_t au_offset, h_offset;
 } mok_saved_layout;
 
+/* MXFP8 workspaces (for inspection): byte offsets of the quantised GEMM operands.
+ * Forward slot m % ring starts at m % ring * fwd_slot in fwd_ws: xq [T][H] with scales
+ * xs [H/128][T][4], hq [R][I] with hs [I/128][R][4].  Backward slot: dyq [T][H] with dys
+ * [H/128][T][4], dguq [R][2I] with dgus [2I/128][R][4].  The weight-gradient stash in
+ * bwd_ws holds bf16 rows in routed order, micro-batch m at rows m*R..: st_xs [M*R][H]
+ * (x), st_dos [M*R][H] (dO = g*dy), st_h [M*R][I], st_dgu [M*R][2I].  After a flush
+ * bwd_ws holds pofs[E+1] int32 (first padded row of each expert's segment, pofs[E] =
+ * rows used) and the token-axis operands, feature-major over kmax padded rows:
+ * dot [H][kmax] (dO), ht [I][kmax], dgut [2I][kmax], xt [H][kmax], each with
+ * scales [kmax/128][F][4] (F = its feature count). */
+typedef struct mok_mx_layout {
+  size_t fwd_slot, xq, xs, hq, hs;
+  size_t bwd_slot, dyq, dys, dguq, dgus;
+  size_t st_xs, st_dos, st_h, st_dgu;
+  size_t pofs, dot, dots, ht, hts, dgut, dguts, xt, xts;
+  int64_t kmax;
+} mok_mx_layout;
+
 /* Fill *sizes for descriptor d.  Pure host computation. */
 mok_status mok_workspace_query(const mok_desc* d, mok_sizes* sizes);
 mok_status mok_schedule_layout_query(const mok_desc* d, mok_schedule_layout* layout);
 mok_status mok_saved_layout_query(const mok_desc* d, mok_saved_layout* layout);
+/* MOK_ERR_DTYPE unless gemm = MOK_MXFP8. */
+mok_status mok_mx_layout_query(const mok_desc* d, mok_mx_layout* layout);
 
 /*
  * mok_route -- top-k router gating (kwkr.cn explainer, section 4.1).
@@ -201,10 +239,12 @@ mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const flo
  * expert: counts, offsets, perm, inv, then the tile list.  Integer-exact and
  * independent of launch order.  idx [T][k] int32 with values in [0, E)
  * (values outside that range are a caller error and give an unspecified
- * schedule); sched has mok_sizes.sched bytes.  The number of tiles stays on
- * the device: the GEMM kernels read it there.
+ * schedule); sched has sched_bytes >= mok_sizes.sched bytes (else
+ * MOK_ERR_WORKSPACE).  The header is stamped with the descriptor's hash and
+ * status MOK_OK.  The number of tiles stays on the device: the GEMM kernels
+ * read it there.
  */
-mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched, void* stream);
+mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched, size_t sched_bytes, void* stream);
 
 /*
  * mok_moe_forward -- pull dispatch, grouped SwiGLU expert FFN, push combine.
@@ -212,13 +252,16 @@ mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched
  *   a = W1[e][0:I].x_t, u = W1[e][I:2I].x_t  (gathered straight into LDS),
  *   h = silu(a)*u, o = W2[e].h  -> partial row s (rounded to `act`),
  *   y_t = sum_{j=0..k-1} gate[t][j] * partial[t*k+j]   (fp32, slot order).
- * Writes y [T][H], saved (mok_saved_layout), uses ws (mok_sizes.fwd_ws).
+ * Writes y [T][H], saved (saved_bytes >= mok_sizes.saved, layout
+ * mok_saved_layout), uses ws (ws_bytes >= mok_sizes.fwd_ws); smaller buffers give
+ * MOK_ERR_WORKSPACE.  sched is the table mok_schedule_build made for the same
+ * descriptor (else nothing is written but its status word, see "Schedule check").
  * MXFP8: x rows and h rows are quantised along K inside the call (h in the fc1
  * epilogue, from its bf16 value); w->mx supplies w1q/w1s and w2q/w2s.  Each
  * micro-batch needs its own `saved` buffer until its backward call.
  */
-mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, const float* gate,
-                           const mok_weights* w, void* y, void* saved, void* ws, void* stream);
+mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const float* gate, const mok_weights* w,
+                           void* y, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mok_moe_backward -- gradients of L = <dy, y>.
@@ -246,24 +289,40 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
  * order, which is token order -- so the result equals that of one call over the
  * whole step; every micro-batch must have been stashed by a call since the
  * previous such call.  With MOK_FLAG_WGRAD_DEFER, dw1/dw2/dwr may be NULL.
+ * saved_bytes >= mok_sizes.saved and ws_bytes >= mok_sizes.bwd_ws, else
+ * MOK_ERR_WORKSPACE; the schedule check is as for mok_moe_forward.
  */
-mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x, const int32_t* idx,
-                            const float* gate, const mok_weights* w, const void* wr, const void* saved,
+mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const int32_t* idx, const float* gate,
+                            const mok_weights* w, const void* wr, const void* saved, size_t saved_bytes,
                             const void* dy, void* dx, void* dw1, void* dw2, float* dgate, void* dwr, void* ws,
-                            void* stream);
+                            size_t ws_bytes, void* stream);
 
 /*
- * Measurement aid (process-wide state, not thread-safe). While set, every
- * launch of the kernel group `name` -- one of "route", "schedule", "fc1",
- * "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "gather", "dw2",
- * "dw1", "dwr", and for MXFP8 "quant" (row quantisers and stash copies),
- * "flush" (block table and token-axis quantisers), or "*" for all -- is bracketed by hipEventRecord(events[2n]) before
- * and hipEventRecord(events[2n+1]) after it on the launch stream, for
- * n = 0, 1, ... < capacity; later launches are not bracketed.  `events` are
- * caller-created hipEvent_t handles.  name == NULL ends tracing.  The trace
- * never synchronises; elapsed times are read by the caller.
+ * Measurement aid.  The caller owns a mok_trace and binds it to the calling
+ * thread with mok_trace_bind; the library keeps only that thread-local pointer
+ * (no state shared between threads).  While bound, every launch made by this
+ * thread's calls of the kernel group `filter` -- one of "route", "schedule",
+ * "fc1", "fc2", "combine", "dh", "router_bwd", "dx", "dx_reduce", "gather",
+ * "dw2", "dw1", "dwr", and for MXFP8 "quant" (row quantisers and stash
+ * copies), "flush" (block table and token-axis quantisers), or "*" for all --
+ * is bracketed by hipEventRecord(events[2n]) before and
+ * hipEventRecord(events[2n+1]) after it on the launch stream, for
+ * n = count, count + 1, ... < capacity (later launches are not bracketed);
+ * names[n] receives the group's static name and count is advanced.
+ * `events` are caller-created hipEvent_t handles.  The trace never
+ * synchronises; elapsed times are read by the caller.
  */
-mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity);
+#define MOK_TRACE_MAX 4096
+typedef struct mok_trace {
+  const char* filter;               /* kernel group or "*" (caller-owned string)  */
+  void* const* events;              /* 2 * capacity hipEvent_t handles             */
+  int32_t capacity;                 /* 0 .. MOK_TRACE_MAX                          */
+  int32_t count;                    /* launches bracketed so far (library-written) */
+  const char* names[MOK_TRACE_MAX]; /* group of each bracketed launch              */
+} mok_trace;
+/* Bind t to the calling thread (NULL unbinds).  MOK_ERR_SHAPE if capacity is out of
+ * range, MOK_ERR_NULL if filter or events is NULL. */
+mok_status mok_trace_bind(mok_trace* t);
 /*
  * mok_weights_quantize -- the MXFP8 orientations of bf16 expert weights w1
  * [E][2I][H] and w2 [E][H][I] (see mok_mx_weights for shapes): w1q/w2q quantise
@@ -275,11 +334,6 @@ mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity
  */
 mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w2, const mok_mx_weights* out,
                                 void* stream);
-
-/* Launches bracketed since the last mok_trace_set. */
-int32_t mok_trace_count(void);
-/* Kernel group of the n-th bracketed launch (static string), or NULL. */
-const char* mok_trace_name(int32_t n);
 
 /* Static string naming a status code. */
 const char* mok_status_string(mok_status s);

@@ -1,6 +1,6 @@
 // C-ABI entry points of libmok: argument checks, buffer layouts, launches.
+#include <cstring>
 #include <mutex>
-#include <string>
 
 #include "kernels.h"
 
@@ -81,7 +81,7 @@ int choose_tile_m(int64_t R, int I, int cus) {
 
 struct Layout {
   int BM = 32, max_tiles = 0;
-  size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, sched;
+  size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, sched;  // header at 0
   size_t au, h, saved;
   size_t fwd_part, fwd;
   size_t dgu, bpart, dgp, dz, xs, dos, bwd;
@@ -96,7 +96,7 @@ Layout layout_of(const mok_desc* d, int BM) {
   L.BM = BM;
   L.max_tiles = (int)(R / BM + std::min<int64_t>(d->E, R));
   const int64_t worst_tiles = R / 32 + std::min<int64_t>(d->E, R);
-  size_t o = 0;
+  size_t o = up(64);  // header int32[16]
   L.counts = o; o = up(o + 4 * (size_t)d->E);
   L.offsets = o; o = up(o + 4 * (size_t)(d->E + 1));
   L.tile_start = o; o = up(o + 4 * (size_t)(d->E + 1));
@@ -193,12 +193,28 @@ mok_status resolve(const mok_desc* d, Layout* L, int* cus) {
   return MOK_OK;
 }
 
+// FNV-1a over the 32-bit words that fix a schedule's meaning: the problem shape and
+// dtypes, the resolved tile height and the tile capacity.
+uint32_t desc_hash(const mok_desc* d, const Layout& L) {
+  const uint32_t w[10] = {(uint32_t)d->T, (uint32_t)(d->T >> 32), (uint32_t)d->H, (uint32_t)d->E, (uint32_t)d->k,
+                          (uint32_t)d->I, (uint32_t)d->act, (uint32_t)d->gemm, (uint32_t)L.BM,
+                          (uint32_t)L.max_tiles};
+  uint32_t h = 2166136261u;
+  for (uint32_t v : w)
+    for (int b = 0; b < 4; ++b) {
+      h ^= (v >> (8 * b)) & 0xFFu;
+      h *= 16777619u;
+    }
+  return h;
+}
+
 mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) {
   Layout L;
   int cus = 0;
   mok_status st = resolve(d, &L, &cus);
   if (st != MOK_OK) return st;
   char* sb = (char*)sched;
+  c->guard = Guard{(int32_t*)sb, desc_hash(d, L)};
   c->T = d->T;
   c->H = d->H;
   c->E = d->E;
@@ -229,34 +245,31 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
     if (!aligned16(p)) return MOK_ERR_ALIGN; \
   } while (0)
 
-// ---- measurement trace (see mok_trace_set) ----
-struct Trace {
-  std::string filter;
-  void* const* events = nullptr;
-  int cap = 0;
-  int count = 0;
-  const char* names[4096];
-};
-Trace g_trace;
+// Buffer sizes passed by the caller against what the descriptor needs.
+mok_status need(size_t have, size_t want) { return have >= want ? MOK_OK : MOK_ERR_WORKSPACE; }
+
+// ---- measurement trace (see mok_trace_bind): the calling thread's caller-owned trace ----
+thread_local mok_trace* t_trace = nullptr;
 
 bool trace_on(const char* name) {
-  return g_trace.events != nullptr && g_trace.count < g_trace.cap &&
-         (g_trace.filter == "*" || g_trace.filter == name);
+  const mok_trace* t = t_trace;
+  return t != nullptr && t->count >= 0 && t->count < t->capacity &&
+         (std::strcmp(t->filter, "*") == 0 || std::strcmp(t->filter, name) == 0);
 }
 
 // Launch `call` (a hipError_t expression) bracketed by trace events when traced.
-#define MOK_LAUNCH(name, stream, call)                                                              \
-  do {                                                                                              \
-    const bool tr_ = trace_on(name);                                                                \
-    if (tr_ && hipEventRecord((hipEvent_t)g_trace.events[2 * g_trace.count], stream) != hipSuccess) \
-      return MOK_ERR_HIP;                                                                           \
-    if ((call) != hipSuccess) return MOK_ERR_HIP;                                                   \
-    if (tr_) {                                                                                      \
-      if (hipEventRecord((hipEvent_t)g_trace.events[2 * g_trace.count + 1], stream) != hipSuccess)  \
-        return MOK_ERR_HIP;                                                                         \
-      if (g_trace.count < 4096) g_trace.names[g_trace.count] = name;                                \
-      ++g_trace.count;                                                                              \
-    }                                                                                               \
+#define MOK_LAUNCH(name, stream, call)                                                          \
+  do {                                                                                          \
+    const bool tr_ = trace_on(name);                                                            \
+    if (tr_ && hipEventRecord((hipEvent_t)t_trace->events[2 * t_trace->count], stream) != hipSuccess) \
+      return MOK_ERR_HIP;                                                                       \
+    if ((call) != hipSuccess) return MOK_ERR_HIP;                                               \
+    if (tr_) {                                                                                  \
+      if (hipEventRecord((hipEvent_t)t_trace->events[2 * t_trace->count + 1], stream) != hipSuccess) \
+        return MOK_ERR_HIP;                                                                     \
+      t_trace->names[t_trace->count] = name;                                                    \
+      ++t_trace->count;                                                                         \
+    }                                                                                           \
   } while (0)
 
 // MXFP8 backward of micro-batch d->mb_index (see mok_moe_backward in mok.h).
@@ -307,13 +320,10 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
     MOK_LAUNCH("quant", c.s, launch_gather_rows(c, dy, gate, wb + X.st_dos + (size_t)(m * R * H * 2)));
     MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_h + (size_t)(m * R * I * 2), sv + L.h, (size_t)(R * I * 2),
                                             hipMemcpyDeviceToDevice, c.s));
-    MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_perm + (size_t)(m * R * 4), c.perm, (size_t)(R * 4),
-                                            hipMemcpyDeviceToDevice, c.s));
   }
-  MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_counts + (size_t)(m * E * 4), c.counts, (size_t)(E * 4),
-                                          hipMemcpyDeviceToDevice, c.s));
-  MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_offsets + (size_t)(m * (E + 1) * 4), c.offsets,
-                                          (size_t)((E + 1) * 4), hipMemcpyDeviceToDevice, c.s));
+  MOK_LAUNCH("quant", c.s, launch_stash_sched(c, (int32_t*)(wb + X.st_counts) + m * E,
+                                              (int32_t*)(wb + X.st_offsets) + m * (E + 1),
+                                              (int32_t*)(wb + X.st_perm) + m * R));
   if (!flush) return MOK_OK;
 
   // weight gradients over the whole step
@@ -369,6 +379,9 @@ mok_status mok_schedule_layout_query(const mok_desc* d, mok_schedule_layout* out
   int cus = 0;
   mok_status st = resolve(d, &L, &cus);
   if (st != MOK_OK) return st;
+  out->status = 4 * kHdrStatus;
+  out->hash = desc_hash(d, L);
+  out->reserved = 0;
   out->counts = L.counts;
   out->offsets = L.offsets;
   out->tile_start = L.tile_start;
@@ -388,6 +401,18 @@ mok_status mok_saved_layout_query(const mok_desc* d, mok_saved_layout* out) {
   const Layout L = layout_of(d, 32);
   out->au_offset = L.au;
   out->h_offset = L.h;
+  return MOK_OK;
+}
+
+mok_status mok_mx_layout_query(const mok_desc* d, mok_mx_layout* out) {
+  mok_status st = check_desc(d);
+  if (st != MOK_OK) return st;
+  if (out == nullptr) return MOK_ERR_NULL;
+  if (!is_mx(d)) return MOK_ERR_DTYPE;
+  const MxLayout X = mx_layout_of(d);
+  *out = mok_mx_layout{X.fslot, X.xq,     X.xs,   X.hq,   X.hs,   X.bslot, X.dyq, X.dys,
+                       X.dguq,  X.dgus,   X.st_xs, X.st_dos, X.st_h, X.st_dgu, X.pofs, X.dot,
+                       X.dots,  X.ht,     X.hts,  X.dgut, X.dguts, X.xt,    X.xts, X.kmax};
   return MOK_OK;
 }
 
@@ -416,22 +441,29 @@ mok_status mok_route(const mok_desc* d, const void* x, const void* wr, const flo
   return MOK_OK;
 }
 
-mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched, void* stream) {
+mok_status mok_schedule_build(const mok_desc* d, const int32_t* idx, void* sched, size_t sched_bytes, void* stream) {
   MOK_REQUIRE(sched);
+  mok_status st = check_desc(d);
+  if (st != MOK_OK) return st;
+  if ((st = need(sched_bytes, layout_of(d, 32).sched)) != MOK_OK) return st;
   Ctx c;
-  mok_status st = make_ctx(d, sched, stream, &c);
+  st = make_ctx(d, sched, stream, &c);
   if (st != MOK_OK) return st;
   if (c.R > 0) MOK_REQUIRE(idx);
   MOK_LAUNCH("schedule", c.s, launch_schedule(c, idx));
   return MOK_OK;
 }
 
-mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, const float* gate,
-                           const mok_weights* w, void* y, void* saved, void* ws, void* stream) {
+mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const float* gate, const mok_weights* w,
+                           void* y, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
   MOK_REQUIRE(sched);
   if (w == nullptr) return MOK_ERR_NULL;
+  mok_sizes need_sz;
+  mok_status st = mok_workspace_query(d, &need_sz);
+  if (st != MOK_OK) return st;
+  if ((st = need(saved_bytes, need_sz.saved)) != MOK_OK || (st = need(ws_bytes, need_sz.fwd_ws)) != MOK_OK) return st;
   Ctx c;
-  mok_status st = make_ctx(d, sched, stream, &c);
+  st = make_ctx(d, sched, stream, &c);
   if (st != MOK_OK) return st;
   if (c.R == 0) return MOK_OK;
   MOK_REQUIRE(x);
@@ -465,14 +497,18 @@ mok_status mok_moe_forward(const mok_desc* d, const void* sched, const void* x, 
   return MOK_OK;
 }
 
-mok_status mok_moe_backward(const mok_desc* d, const void* sched, const void* x, const int32_t* idx,
-                            const float* gate, const mok_weights* w, const void* wr, const void* saved,
+mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const int32_t* idx, const float* gate,
+                            const mok_weights* w, const void* wr, const void* saved, size_t saved_bytes,
                             const void* dy, void* dx, void* dw1, void* dw2, float* dgate, void* dwr, void* ws,
-                            void* stream) {
+                            size_t ws_bytes, void* stream) {
   MOK_REQUIRE(sched);
   if (w == nullptr) return MOK_ERR_NULL;
+  mok_sizes need_sz;
+  mok_status st = mok_workspace_query(d, &need_sz);
+  if (st != MOK_OK) return st;
+  if ((st = need(saved_bytes, need_sz.saved)) != MOK_OK || (st = need(ws_bytes, need_sz.bwd_ws)) != MOK_OK) return st;
   Ctx c;
-  mok_status st = make_ctx(d, sched, stream, &c);
+  st = make_ctx(d, sched, stream, &c);
   if (st != MOK_OK) return st;
   if (is_mx(d)) return mx_backward(d, c, x, idx, gate, w, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws);
   MOK_REQUIRE(dw1);
@@ -546,24 +582,16 @@ mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w
   return MOK_OK;
 }
 
-mok_status mok_trace_set(const char* name, void* const* events, int32_t capacity) {
-  if (name == nullptr) {
-    g_trace.events = nullptr;
-    g_trace.cap = 0;
+mok_status mok_trace_bind(mok_trace* t) {
+  if (t == nullptr) {
+    t_trace = nullptr;
     return MOK_OK;
   }
-  if (events == nullptr) return MOK_ERR_NULL;
-  if (capacity < 0) return MOK_ERR_SHAPE;
-  g_trace.filter = name;
-  g_trace.events = events;
-  g_trace.cap = std::min(capacity, 4096);
-  g_trace.count = 0;
+  if (t->filter == nullptr || t->events == nullptr) return MOK_ERR_NULL;
+  if (t->capacity < 0 || t->capacity > MOK_TRACE_MAX || t->count < 0) return MOK_ERR_SHAPE;
+  t_trace = t;
   return MOK_OK;
 }
-
-int32_t mok_trace_count(void) { return g_trace.count; }
-
-const char* mok_trace_name(int32_t n) { return (n >= 0 && n < g_trace.count && n < 4096) ? g_trace.names[n] : nullptr; }
 
 const char* mok_status_string(mok_status s) {
   switch (s) {
@@ -573,10 +601,12 @@ const char* mok_status_string(mok_status s) {
     case MOK_ERR_SHAPE: return "descriptor size out of range";
     case MOK_ERR_DTYPE: return "unsupported dtype combination";
     case MOK_ERR_HIP: return "HIP call failed";
+    case MOK_ERR_WORKSPACE: return "caller buffer smaller than the descriptor needs";
+    case MOK_ERR_SCHEDULE_MISMATCH: return "schedule built for another descriptor";
   }
   return "unknown status";
 }
 
-int32_t mok_version(void) { return 201; }
+int32_t mok_version(void) { return 300; }
 
 }  // extern "C"

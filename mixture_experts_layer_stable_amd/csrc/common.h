@@ -88,6 +88,28 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Schedule header check. mok_schedule_build writes, at the start of the schedule
+// buffer, the hash of the descriptor it was built for (word 1) and a status word
+// (word 4). A kernel that consumes the schedule (or runs as part of a call that
+// does) compares the hash with the one of its own descriptor first: on a mismatch
+// every workgroup leaves MOK_ERR_SCHEDULE_MISMATCH in the status word (all write
+// the same value) and exits before touching anything else, so a table built for
+// another problem never indexes memory. The test is uniform over the workgroup.
+// hdr == nullptr: no schedule involved (weight quantisation), never fails.
+constexpr int kHdrHash = 1, kHdrStatus = 4;
+
+struct Guard {
+  int32_t* hdr;
+  uint32_t expect;
+};
+
+__device__ __forceinline__ bool guard_fail(const Guard& g) {
+  if (g.hdr == nullptr) return false;
+  if ((uint32_t)g.hdr[kHdrHash] == g.expect) return false;
+  if (threadIdx.x == 0) g.hdr[kHdrStatus] = MOK_ERR_SCHEDULE_MISMATCH;
+  return true;
+}
+
 // Logical workgroup index with consecutive indices on one XCD: the dispatcher
 // places workgroup b on XCD b % 8, so b -> (b % 8) * ceil(G/8) + b / 8 gives
 // each XCD a contiguous range (G need not be a multiple of 8).

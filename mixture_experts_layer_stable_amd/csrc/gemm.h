@@ -262,6 +262,7 @@ struct Sched {
   const int32_t* perm;
   int E;
   int BM;
+  Guard guard;
 };
 
 // Persistent walk over the tiles of a row GEMM (M = routed rows of one
@@ -304,9 +305,12 @@ __device__ __forceinline__ void for_each_row_tile(const Sched& sc, const int* s_
   }
 }
 
-// Load tile_start[0..E] into LDS (called once per persistent kernel).
+// Load tile_start[0..E] into LDS (called once per persistent kernel). When the
+// schedule check fails every entry is 0: the tile walk then visits no tile and the
+// kernel exits having written nothing.
 __device__ __forceinline__ void load_tile_start(const Sched& sc, int* s_ts) {
-  for (int i = threadIdx.x; i <= sc.E; i += blockDim.x) s_ts[i] = sc.tile_start[i];
+  const bool bad = guard_fail(sc.guard);
+  for (int i = threadIdx.x; i <= sc.E; i += blockDim.x) s_ts[i] = bad ? 0 : sc.tile_start[i];
   __syncthreads();
 }
 

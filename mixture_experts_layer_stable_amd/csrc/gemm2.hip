@@ -172,6 +172,7 @@ struct DwArgs2 {
   void* out;
   int M, N;           // dw2: H, I; dw1: 2I, H
   int lda, ldb;       // elements per routed row of arows / brows
+  Guard guard;
 };
 
 template <class Tl, typename TO>
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  if (guard_fail(a.guard)) return;
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const int e = L / (MT * NT);
   const int rem = L - e * MT * NT;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   const int li = blockIdx.x / P;
   const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
   int64_t L = lo + li;
-  if (L >= hi) return;
+  if (L >= hi || guard_fail(a.guard)) return;
   OA oa;
   OB ob;
   int e = 0, mt = 0, nt = 0, KT = 0;
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
 }
 
 // ---------------------------------------------------------------------------
-static Sched sched_of2(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+static Sched sched_of2(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM, c.guard}; }
 
 template <int KIND, int BM, int BN>
 static hipError_t row_launch(const Ctx& c, const RowArgs& a, int N) {
@@ -374,12 +376,12 @@ static hipError_t dw_any2(const Ctx& c, const DwArgs2& a) {
 }
 
 hipError_t launch_dw2_bf16(const Ctx& c, const void* dos, const void* h, void* dw2) {
-  DwArgs2 a{c.counts, c.offsets, (const bf16*)dos, (const bf16*)h, dw2, c.H, c.I, c.H, c.I};
+  DwArgs2 a{c.counts, c.offsets, (const bf16*)dos, (const bf16*)h, dw2, c.H, c.I, c.H, c.I, c.guard};
   return dw_any2(c, a);
 }
 
 hipError_t launch_dw1_bf16(const Ctx& c, const void* dgu, const void* xs, void* dw1) {
-  DwArgs2 a{c.counts, c.offsets, (const bf16*)dgu, (const bf16*)xs, dw1, 2 * c.I, c.H, 2 * c.I, c.H};
+  DwArgs2 a{c.counts, c.offsets, (const bf16*)dgu, (const bf16*)xs, dw1, 2 * c.I, c.H, 2 * c.I, c.H, c.guard};
   return dw_any2(c, a);
 }
 

@@ -154,6 +154,7 @@ struct DwArgs {
   const T* rows;       // routed-row operand (h for dW2 [R][I], dGU for dW1 [R][2I])
   TO* out;
   int H, I, k;
+  Guard guard;
 };
 
 // (g*dY)[row] or dY[row] / x[row] read through the permutation (token-major operand).
@@ -202,6 +203,7 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs<T, TO> a) {
   const int M = IS_DW2 ? a.H : 2 * a.I;
   const int N = IS_DW2 ? a.I : a.H;
   const int MT = M / Tl::BM, NT = N / Tl::BN;
+  if (guard_fail(a.guard)) return;
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const int e = L / (MT * NT);
   const int rem = L - e * MT * NT;
@@ -247,7 +249,7 @@ static int persistent_grid_b(const Ctx& c, int ntn) {
   return g;
 }
 
-static Sched sched_of_b(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+static Sched sched_of_b(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM, c.guard}; }
 
 template <typename T, int BM, int BN>
 static hipError_t dh_t(const Ctx& c, const void* dy, const void* w2, const void* au, const void* h, const float* gate,
@@ -305,7 +307,7 @@ hipError_t launch_dx(const Ctx& c, const void* dgu, const void* w1, void* part) 
 template <typename T, typename TO, bool IS_DW2>
 static hipError_t dw_t(const Ctx& c, const T* tok, const float* gate, const T* rows, void* out) {
   using Tl = DwTiling;
-  DwArgs<T, TO> a{c.counts, c.offsets, c.perm, tok, gate, rows, (TO*)out, c.H, c.I, c.k};
+  DwArgs<T, TO> a{c.counts, c.offsets, c.perm, tok, gate, rows, (TO*)out, c.H, c.I, c.k, c.guard};
   const int M = IS_DW2 ? c.H : 2 * c.I, N = IS_DW2 ? c.I : c.H;
   const int64_t blocks = (int64_t)c.E * (M / Tl::BM) * (N / Tl::BN);
   hipLaunchKernelGGL((dw_kernel<T, TO, Tl, IS_DW2>), dim3((unsigned)blocks), dim3(kThreads), 0, c.s, a);

@@ -126,7 +126,7 @@ static int persistent_grid(const Ctx& c, int ntn) {
   return g;
 }
 
-static Sched sched_of(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+static Sched sched_of(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM, c.guard}; }
 
 template <typename T, int BM>
 static hipError_t fc1_bm(const Ctx& c, const void* x, const void* w1, void* au, void* h) {

@@ -322,6 +322,7 @@ struct MxDwArgs {
   void* out;
   int M, N;
   int64_t kld;
+  Guard guard;
 };
 
 template <class Tl, typename TO>
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  if (guard_fail(a.guard)) return;
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const int e = L / (MT * NT);
   const int rem = L - e * MT * NT;
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   const int li = blockIdx.x / P;
   const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
   int64_t L = lo + li;
-  if (L >= hi) return;
+  if (L >= hi || guard_fail(a.guard)) return;
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
   const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
   OA oa;
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
 }
 
 // ---------------------------------------------------------------------------
-static Sched sched_of_mx(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM}; }
+static Sched sched_of_mx(const Ctx& c) { return Sched{c.counts, c.offsets, c.tile_start, c.perm, c.E, c.BM, c.guard}; }
 
 template <int KIND, int BM, int BN>
 static hipError_t row_launch_mx(const Ctx& c, const MxRowArgs& a, int N) {
@@ -532,16 +534,14 @@ static hipError_t dw_launch_mx(const Ctx& c, const MxDwArgs& a) {
     hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
     return hipGetLastError();
   }
-  if (c.wgrad_f32)
-    hipLaunchKernelGGL((dw_mx_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
-  else
-    hipLaunchKernelGGL((dw_mx_kernel<Tl, bf16>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
+  hipLaunchKernelGGL((dw_mx_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const void* as, const void* bq,
                         const void* bs, void* out, int M, int N, int64_t kld) {
-  MxDwArgs a{pofs, (const uint8_t*)aq, (const uint8_t*)as, (const uint8_t*)bq, (const uint8_t*)bs, out, M, N, kld};
+  MxDwArgs a{pofs, (const uint8_t*)aq, (const uint8_t*)as, (const uint8_t*)bq, (const uint8_t*)bs, out, M, N, kld,
+              c.guard};
   if (N % 256 == 0) return dw_launch_mx<Tiling<128, 256, 2, 4>>(c, a);
   return dw_launch_mx<Tiling<128, 128, 2, 2>>(c, a);
 }

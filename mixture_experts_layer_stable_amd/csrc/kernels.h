@@ -17,6 +17,7 @@ struct Ctx {
   int grid;        // persistent GEMM grid
   int gemm;        // expert-GEMM dtype (mok_dtype)
   hipStream_t s;
+  Guard guard;     // schedule header check (every kernel of forward/backward)
   // schedule table (device)
   int32_t* counts;
   int32_t* offsets;
@@ -29,7 +30,11 @@ struct Ctx {
 
 hipError_t launch_route(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
                         float* logits);
+// builds the table and stamps the header (hash c.guard.expect, status MOK_OK)
 hipError_t launch_schedule(const Ctx& c, const int32_t* idx);
+// stash copy of a micro-batch's counts, offsets (E+1) and perm (R); zero counts and
+// offsets (nothing else) when the schedule check fails
+hipError_t launch_stash_sched(const Ctx& c, int32_t* counts, int32_t* offsets, int32_t* perm);
 
 hipError_t launch_fc1(const Ctx& c, const void* x, const void* w1, void* au, void* h);
 hipError_t launch_fc2(const Ctx& c, const void* h, const void* w2, void* part);

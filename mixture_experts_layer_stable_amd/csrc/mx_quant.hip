@@ -27,11 +27,11 @@ static unsigned nblk(int64_t n, int b = 256) { return (unsigned)((n + b - 1) / b
 // Scale byte of block b (32 features) of row r: row-major (kmaj_rows = 0) at
 // r * F/32 + b; K-tile-major (kmaj_rows > 0 = rows per matrix) at
 // [z][b/4][r % kmaj_rows][b % 4] with z = r / kmaj_rows.
-__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restrict__ src, int64_t nvec,
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(Guard gd, const bf16* __restrict__ src, int64_t nvec,
                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s, int F,
                                                             int64_t kmaj_rows) {
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= nvec) return;  // nvec and blockDim are even: a pair leaves together
+  if (guard_fail(gd) || v >= nvec) return;  // nvec and blockDim are even: a pair leaves together
   float f[16];
   load16<bf16>(src + v * 16, f);
   uint32_t sb;
@@ -51,7 +51,7 @@ hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int
                                 int64_t kmaj_rows) {
   const int64_t nvec = rows * (F / 16);
   if (nvec == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(nblk(nvec)), dim3(256), 0, c.s, (const bf16*)src, nvec, (uint8_t*)q,
+  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(nblk(nvec)), dim3(256), 0, c.s, c.guard, (const bf16*)src, nvec, (uint8_t*)q,
                      (uint8_t*)s, F, kmaj_rows);
   return hipGetLastError();
 }
@@ -78,12 +78,13 @@ struct ColQuantArgs {
   int64_t out_ld;
   uint8_t* q;
   uint8_t* s;
+  Guard guard;
 };
 
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
   __shared__ float tile[128][65];
   const int r0 = blockIdx.x * 128, f0 = blockIdx.y * 64, z = blockIdx.z;
-  if (a.kdev != nullptr && r0 >= *a.kdev) return;
+  if (guard_fail(a.guard) || (a.kdev != nullptr && r0 >= *a.kdev)) return;
   const bf16* src = a.src + (int64_t)z * a.src_mat;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -127,15 +128,17 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
 hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, int64_t ld, const int32_t* rowmap,
                                 const int32_t* kdev, int K, int F, int mats, int64_t out_ld, void* q, void* s) {
   if (K == 0 || F == 0 || mats == 0) return hipSuccess;
-  ColQuantArgs a{(const bf16*)src, src_mat, ld, rowmap, kdev, F, out_ld, (uint8_t*)q, (uint8_t*)s};
+  ColQuantArgs a{(const bf16*)src, src_mat, ld, rowmap, kdev, F, out_ld, (uint8_t*)q, (uint8_t*)s, c.guard};
   hipLaunchKernelGGL(mx_quant_cols_kernel, dim3(K / 128, F / 64, mats), dim3(256), 0, c.s, a);
   return hipGetLastError();
 }
 
 // One workgroup of 1024 threads (E <= 1024). counts is [M][E].
-__global__ __launch_bounds__(1024) void mx_flush_table_kernel(const int32_t* __restrict__ counts, int M, int E,
-                                                              int32_t* __restrict__ gcnt, int32_t* __restrict__ pofs) {
+__global__ __launch_bounds__(1024) void mx_flush_table_kernel(Guard gd, const int32_t* __restrict__ counts, int M,
+                                                              int E, int32_t* __restrict__ gcnt,
+                                                              int32_t* __restrict__ pofs) {
   __shared__ int sc[1024];
+  if (guard_fail(gd)) return;
   const int e = threadIdx.x;
   int c = 0;
   if (e < E)
@@ -157,13 +160,13 @@ __global__ __launch_bounds__(1024) void mx_flush_table_kernel(const int32_t* __r
 }
 
 // offsets is [M][E+1]; one thread per padded row p < kmax.
-__global__ __launch_bounds__(256) void mx_rowmap_kernel(const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(256) void mx_rowmap_kernel(Guard gd, const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets, int M, int E, int R,
                                                         const int32_t* __restrict__ gcnt,
                                                         const int32_t* __restrict__ pofs, int64_t kmax,
                                                         int32_t* __restrict__ rowmap) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= kmax || p >= pofs[E]) return;
+  if (guard_fail(gd) || p >= kmax || p >= pofs[E]) return;
   int lo = 0, hi = E;  // pofs[lo] <= p < pofs[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -187,9 +190,9 @@ __global__ __launch_bounds__(256) void mx_rowmap_kernel(const int32_t* __restric
 
 hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int32_t* offsets, int M, int32_t* gcnt,
                                  int32_t* pofs, int64_t kmax, int32_t* rowmap) {
-  hipLaunchKernelGGL(mx_flush_table_kernel, dim3(1), dim3(1024), 0, c.s, counts, M, c.E, gcnt, pofs);
+  hipLaunchKernelGGL(mx_flush_table_kernel, dim3(1), dim3(1024), 0, c.s, c.guard, counts, M, c.E, gcnt, pofs);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL(mx_rowmap_kernel, dim3(nblk(kmax)), dim3(256), 0, c.s, counts, offsets, M, c.E, c.R, gcnt, pofs,
+  hipLaunchKernelGGL(mx_rowmap_kernel, dim3(nblk(kmax)), dim3(256), 0, c.s, c.guard, counts, offsets, M, c.E, c.R, gcnt, pofs,
                      kmax, rowmap);
   return hipGetLastError();
 }
@@ -202,7 +205,7 @@ hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int3
 // spread over kDwrChunks threads per column.
 constexpr int kDwrChunks = 8;
 
-__global__ __launch_bounds__(256) void dwr_stash_part_kernel(const float* __restrict__ dz,
+__global__ __launch_bounds__(256) void dwr_stash_part_kernel(Guard gd, const float* __restrict__ dz,
                                                              const int32_t* __restrict__ perm,
                                                              const bf16* __restrict__ xs,
                                                              const int32_t* __restrict__ gcnt,
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) void dwr_stash_part_kernel(const float* __rest
                                                              float* __restrict__ part, int E, int H, int R) {
   const int vpr = H / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)E * kDwrChunks * vpr) return;
+  if (guard_fail(gd) || gid >= (int64_t)E * kDwrChunks * vpr) return;
   const int h0 = (int)(gid % vpr) * 8;
   const int64_t ec = gid / vpr;
   const int c = (int)(ec % kDwrChunks), e = (int)(ec / kDwrChunks);
@@ -236,10 +239,10 @@ __global__ __launch_bounds__(256) void dwr_stash_part_kernel(const float* __rest
 }
 
 template <typename TO>
-__global__ __launch_bounds__(256) void dwr_stash_sum_kernel(const float* __restrict__ part, TO* __restrict__ dwr,
-                                                            int E, int H) {
+__global__ __launch_bounds__(256) void dwr_stash_sum_kernel(Guard gd, const float* __restrict__ part,
+                                                            TO* __restrict__ dwr, int E, int H) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)E * H) return;
+  if (guard_fail(gd) || gid >= (int64_t)E * H) return;
   const int64_t e = gid / H, h = gid % H;
   float s = 0.0f;
 #pragma unroll
@@ -250,14 +253,14 @@ __global__ __launch_bounds__(256) void dwr_stash_sum_kernel(const float* __restr
 hipError_t launch_dwr_stash(const Ctx& c, const float* dz, const int32_t* perm, const void* xs, const int32_t* gcnt,
                             const int32_t* pofs, const int32_t* rowmap, float* part, void* dwr) {
   const int64_t n = (int64_t)c.E * kDwrChunks * (c.H / 8);
-  hipLaunchKernelGGL(dwr_stash_part_kernel, dim3(nblk(n)), dim3(256), 0, c.s, dz, perm, (const bf16*)xs, gcnt, pofs,
+  hipLaunchKernelGGL(dwr_stash_part_kernel, dim3(nblk(n)), dim3(256), 0, c.s, c.guard, dz, perm, (const bf16*)xs, gcnt, pofs,
                      rowmap, part, c.E, c.H, c.R);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int64_t m = (int64_t)c.E * c.H;
   if (c.wgrad_f32)
-    hipLaunchKernelGGL((dwr_stash_sum_kernel<float>), dim3(nblk(m)), dim3(256), 0, c.s, part, (float*)dwr, c.E, c.H);
+    hipLaunchKernelGGL((dwr_stash_sum_kernel<float>), dim3(nblk(m)), dim3(256), 0, c.s, c.guard, part, (float*)dwr, c.E, c.H);
   else
-    hipLaunchKernelGGL((dwr_stash_sum_kernel<bf16>), dim3(nblk(m)), dim3(256), 0, c.s, part, (bf16*)dwr, c.E, c.H);
+    hipLaunchKernelGGL((dwr_stash_sum_kernel<bf16>), dim3(nblk(m)), dim3(256), 0, c.s, c.guard, part, (bf16*)dwr, c.E, c.H);
   return hipGetLastError();
 }
 

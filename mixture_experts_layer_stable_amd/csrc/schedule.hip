@@ -10,9 +10,25 @@
 //   3. rank:   one wave per expert scans idx again in ascending slot order; a
 //              slot's row is offsets[e] + number of earlier slots of e
 //              (ballot + popcount), giving perm (row -> slot) and inv.
+// The scan step also stamps the header (descriptor hash, tile height, tile
+// capacity, status MOK_OK) that the forward and backward kernels check.
 #include "kernels.h"
 
 namespace mok {
+
+struct Stamp {
+  int32_t* hdr;
+  uint32_t hash;
+  int tile_m, max_tiles;
+};
+
+__device__ __forceinline__ void stamp_header(const Stamp& st) {
+  st.hdr[0] = 0x4D4F4B53;
+  st.hdr[kHdrHash] = (int32_t)st.hash;
+  st.hdr[2] = st.tile_m;
+  st.hdr[3] = st.max_tiles;
+  st.hdr[kHdrStatus] = MOK_OK;
+}
 
 __global__ __launch_bounds__(64) void sched_count_kernel(const int32_t* __restrict__ idx, int R,
                                                          int32_t* __restrict__ counts) {
@@ -61,7 +77,8 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
 __global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restrict__ counts, int E, int R, int BM,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_start,
-                                                          int32_t* __restrict__ num_tiles, int4* __restrict__ tiles) {
+                                                          int32_t* __restrict__ num_tiles, int4* __restrict__ tiles,
+                                                          Stamp st) {
   __shared__ int s_wave[17];
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
@@ -78,6 +95,7 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restr
     offsets[E] = R;
     tile_start[E] = tot_t;
     *num_tiles = tot_t;
+    stamp_header(st);
   }
 }
 
@@ -129,7 +147,8 @@ __global__ __launch_bounds__(1024) void sched_fused_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ tile_start,
                                                            int32_t* __restrict__ num_tiles, int4* __restrict__ tiles,
-                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                           Stamp st) {
   __shared__ int s_idx[kSchedFusedMaxR];
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1024];
@@ -162,6 +181,7 @@ __global__ __launch_bounds__(1024) void sched_fused_kernel(const int32_t* __rest
     offsets[E] = R;
     tile_start[E] = tot_t;
     *num_tiles = tot_t;
+    stamp_header(st);
   }
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -183,15 +203,39 @@ __global__ __launch_bounds__(1024) void sched_fused_kernel(const int32_t* __rest
 }
 
 hipError_t launch_schedule(const Ctx& c, const int32_t* idx) {
+  const Stamp st{c.guard.hdr, c.guard.expect, c.BM, c.max_tiles};
   if (c.R <= kSchedFusedMaxR && c.E <= 1024 && (int64_t)c.R * c.E <= (int64_t)1 << 14) {
     hipLaunchKernelGGL(sched_fused_kernel, dim3(1), dim3(1024), 0, c.s, idx, c.R, c.E, c.BM, c.counts, c.offsets,
-                       c.tile_start, c.num_tiles, c.tiles, c.perm, c.inv);
+                       c.tile_start, c.num_tiles, c.tiles, c.perm, c.inv, st);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(sched_count_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.counts);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, c.s, c.counts, c.E, c.R, c.BM, c.offsets,
-                     c.tile_start, c.num_tiles, c.tiles);
+                     c.tile_start, c.num_tiles, c.tiles, st);
   if (c.R > 0) hipLaunchKernelGGL(sched_rank_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.offsets, c.perm, c.inv);
+  return hipGetLastError();
+}
+
+// Copy of one micro-batch's counts, offsets and perm into the weight-gradient stash.
+// With a failed schedule check the stash gets zero counts and offsets, so that a later
+// flush treats the micro-batch as empty instead of reading through stale rows.
+__global__ __launch_bounds__(256) void stash_sched_kernel(Guard gd, const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ perm, int E, int R,
+                                                          int32_t* __restrict__ st_counts,
+                                                          int32_t* __restrict__ st_offsets,
+                                                          int32_t* __restrict__ st_perm) {
+  const bool bad = guard_fail(gd);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < E) st_counts[i] = bad ? 0 : counts[i];
+  if (i <= E) st_offsets[i] = bad ? 0 : offsets[i];
+  if (!bad && i < R) st_perm[i] = perm[i];
+}
+
+hipError_t launch_stash_sched(const Ctx& c, int32_t* counts, int32_t* offsets, int32_t* perm) {
+  const int64_t n = std::max<int64_t>(c.R, (int64_t)c.E + 1);
+  hipLaunchKernelGGL(stash_sched_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.s, c.guard, c.counts,
+                     c.offsets, c.perm, c.E, c.R, counts, offsets, perm);
   return hipGetLastError();
 }
 

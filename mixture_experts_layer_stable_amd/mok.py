@@ -24,7 +24,9 @@ DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8}
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
 STATUS = {0: "MOK_OK", 1: "MOK_ERR_NULL", 2: "MOK_ERR_ALIGN", 3: "MOK_ERR_SHAPE", 4: "MOK_ERR_DTYPE",
-          5: "MOK_ERR_HIP"}
+          5: "MOK_ERR_HIP", 6: "MOK_ERR_WORKSPACE", 7: "MOK_ERR_SCHEDULE_MISMATCH"}
+ERR_WORKSPACE, ERR_SCHEDULE_MISMATCH = 6, 7
+TRACE_MAX = 4096
 
 
 class MokError(RuntimeError):
@@ -57,13 +59,27 @@ class _Sizes(ctypes.Structure):
 
 
 class _SchedLayout(ctypes.Structure):
-    _fields_ = [("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t), ("tile_start", ctypes.c_size_t),
-                ("num_tiles", ctypes.c_size_t), ("perm", ctypes.c_size_t), ("inv", ctypes.c_size_t),
-                ("tiles", ctypes.c_size_t), ("tile_m", ctypes.c_int32), ("max_tiles", ctypes.c_int32)]
+    _fields_ = [("status", ctypes.c_size_t), ("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t),
+                ("tile_start", ctypes.c_size_t), ("num_tiles", ctypes.c_size_t), ("perm", ctypes.c_size_t),
+                ("inv", ctypes.c_size_t), ("tiles", ctypes.c_size_t), ("tile_m", ctypes.c_int32),
+                ("max_tiles", ctypes.c_int32), ("hash", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
+
+
+class _Trace(ctypes.Structure):
+    _fields_ = [("filter", ctypes.c_char_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32), ("names", ctypes.c_char_p * TRACE_MAX)]
 
 
 class _SavedLayout(ctypes.Structure):
     _fields_ = [("au_offset", ctypes.c_size_t), ("h_offset", ctypes.c_size_t)]
+
+
+MX_LAYOUT_FIELDS = ("fwd_slot", "xq", "xs", "hq", "hs", "bwd_slot", "dyq", "dys", "dguq", "dgus", "st_xs", "st_dos",
+                    "st_h", "st_dgu", "pofs", "dot", "dots", "ht", "hts", "dgut", "dguts", "xt", "xts")
+
+
+class _MxLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in MX_LAYOUT_FIELDS] + [("kmax", ctypes.c_int64)]
 
 
 def _load():
@@ -72,15 +88,18 @@ def _load():
                            % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
+    Z = ctypes.c_size_t
     D = ctypes.POINTER(_Desc)
     sig = {
         "mok_workspace_query": [D, ctypes.POINTER(_Sizes)],
         "mok_schedule_layout_query": [D, ctypes.POINTER(_SchedLayout)],
         "mok_saved_layout_query": [D, ctypes.POINTER(_SavedLayout)],
+        "mok_mx_layout_query": [D, ctypes.POINTER(_MxLayout)],
         "mok_route": [D, P, P, P, P, P, P, P],
-        "mok_schedule_build": [D, P, P, P],
-        "mok_moe_forward": [D, P, P, P, ctypes.POINTER(_Weights), P, P, P, P],
-        "mok_moe_backward": [D, P, P, P, P, ctypes.POINTER(_Weights), P, P, P, P, P, P, P, P, P, P],
+        "mok_schedule_build": [D, P, P, Z, P],
+        "mok_moe_forward": [D, P, P, P, ctypes.POINTER(_Weights), P, P, Z, P, Z, P],
+        "mok_moe_backward": [D, P, P, P, P, ctypes.POINTER(_Weights), P, P, Z, P, P, P, P, P, P, P, Z, P],
+        "mok_trace_bind": [ctypes.POINTER(_Trace)],
         "mok_weights_quantize": [D, P, P, ctypes.POINTER(_MxWeights), P],
     }
     for name, args in sig.items():
@@ -91,19 +110,14 @@ def _load():
     lib.mok_status_string.restype = ctypes.c_char_p
     lib.mok_version.argtypes = []
     lib.mok_version.restype = ctypes.c_int32
-    lib.mok_trace_set.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
-    lib.mok_trace_set.restype = ctypes.c_int
-    lib.mok_trace_count.argtypes = []
-    lib.mok_trace_count.restype = ctypes.c_int32
-    lib.mok_trace_name.argtypes = [ctypes.c_int32]
-    lib.mok_trace_name.restype = ctypes.c_char_p
     return lib
 
 
 _lib = _load()
-EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_route",
+EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_mx_layout_query",
+           "mok_route",
            "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_weights_quantize", "mok_status_string",
-           "mok_version", "mok_trace_set", "mok_trace_count", "mok_trace_name")
+           "mok_version", "mok_trace_bind")
 
 
 @dataclass
@@ -149,6 +163,11 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nb(t: Optional[torch.Tensor]) -> int:
+    """Bytes of a buffer tensor (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -176,13 +195,48 @@ def saved_layout_query(d: Desc) -> dict:
     return dict(au_offset=s.au_offset, h_offset=s.h_offset)
 
 
+def mx_layout_query(d: Desc) -> dict:
+    s = _MxLayout()
+    _check(_lib.mok_mx_layout_query(ctypes.byref(d.c()), ctypes.byref(s)), "mok_mx_layout_query")
+    return {n: getattr(s, n) for n, _ in _MxLayout._fields_}
+
+
+def schedule_views(d: Desc, sched) -> dict:
+    """int32 views of the parts of a schedule buffer built for descriptor d (for inspection and tests)."""
+    L = schedule_layout_query(d)
+
+    def iv(off, n):
+        return sched[off: off + 4 * n].view(torch.int32)
+
+    return dict(counts=iv(L["counts"], d.E), offsets=iv(L["offsets"], d.E + 1),
+                tile_start=iv(L["tile_start"], d.E + 1), num_tiles=iv(L["num_tiles"], 1),
+                perm=iv(L["perm"], d.R), inv=iv(L["inv"], d.R),
+                tiles=iv(L["tiles"], 4 * L["max_tiles"]).view(-1, 4), tile_m=L["tile_m"],
+                max_tiles=L["max_tiles"], status=int(iv(L["status"], 1).cpu()[0]))
+
+
 def route(d: Desc, x, wr, bias, idx, gate, logits=None, stream=None):
     _check(_lib.mok_route(ctypes.byref(d.c()), _p(x), _p(wr), _p(bias), _p(idx), _p(gate), _p(logits),
                           _stream(stream)), "mok_route")
 
 
 def schedule_build(d: Desc, idx, sched, stream=None):
-    _check(_lib.mok_schedule_build(ctypes.byref(d.c()), _p(idx), _p(sched), _stream(stream)), "mok_schedule_build")
+    _check(_lib.mok_schedule_build(ctypes.byref(d.c()), _p(idx), _p(sched), _nb(sched), _stream(stream)),
+           "mok_schedule_build")
+
+
+def schedule_status(d: Desc, sched) -> int:
+    """The schedule header's status word (synchronises on the tensor read): MOK_OK, or
+    MOK_ERR_SCHEDULE_MISMATCH once a kernel was handed this table with another descriptor."""
+    off = schedule_layout_query(d)["status"]
+    return int(sched[off: off + 4].view(torch.int32).cpu()[0])
+
+
+def check_schedule(d: Desc, sched, where="schedule"):
+    """Raise MokError if a forward/backward kernel rejected the schedule (after a sync)."""
+    st = schedule_status(d, sched)
+    if st != 0:
+        raise MokError(st, where, _lib.mok_status_string(st).decode())
 
 
 class MxWeights:
@@ -217,19 +271,20 @@ def _weights(w1, w2, mxw):
 def moe_forward(d: Desc, sched, x, gate, w1, w2, y, saved, ws, stream=None, mxw: Optional[MxWeights] = None):
     w, _keep = _weights(w1, w2, mxw)
     _check(_lib.mok_moe_forward(ctypes.byref(d.c()), _p(sched), _p(x), _p(gate), ctypes.byref(w), _p(y), _p(saved),
-                                _p(ws), _stream(stream)), "mok_moe_forward")
+                                _nb(saved), _p(ws), _nb(ws), _stream(stream)), "mok_moe_forward")
 
 
 def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws, stream=None,
                  mxw: Optional[MxWeights] = None):
     w, _keep = _weights(w1, w2, mxw)
     _check(_lib.mok_moe_backward(ctypes.byref(d.c()), _p(sched), _p(x), _p(idx), _p(gate), ctypes.byref(w), _p(wr),
-                                 _p(saved), _p(dy), _p(dx), _p(dw1), _p(dw2), _p(dgate), _p(dwr), _p(ws),
-                                 _stream(stream)), "mok_moe_backward")
+                                 _p(saved), _nb(saved), _p(dy), _p(dx), _p(dw1), _p(dw2), _p(dgate), _p(dwr), _p(ws),
+                                 _nb(ws), _stream(stream)), "mok_moe_backward")
 
 
 class KernelTrace:
-    """Bracket launches of one kernel group (or "*") with HIP events (mok_trace_set).
+    """Bracket launches of one kernel group (or "*") with HIP events (a caller-owned
+    mok_trace bound to this thread with mok_trace_bind).
 
     with KernelTrace("fc1", capacity=64) as tr:
         ... launches ...
@@ -243,18 +298,24 @@ class KernelTrace:
             e.record()
         torch.cuda.synchronize()
         self._handles = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        self._filter = name.encode()
+        self._t = _Trace()
+        self._t.filter = self._filter
+        self._t.events = ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p))
+        self._t.capacity = capacity
+        self._t.count = 0
         self.capacity = capacity
         self.count = 0
         self.names = []
 
     def __enter__(self):
-        _check(_lib.mok_trace_set(self.name.encode(), self._handles, self.capacity), "mok_trace_set")
+        _check(_lib.mok_trace_bind(ctypes.byref(self._t)), "mok_trace_bind")
         return self
 
     def __exit__(self, *exc):
-        self.count = _lib.mok_trace_count()
-        self.names = [_lib.mok_trace_name(i).decode() for i in range(self.count)]
-        _lib.mok_trace_set(None, None, 0)
+        _lib.mok_trace_bind(None)
+        self.count = self._t.count
+        self.names = [self._t.names[i].decode() for i in range(self.count)]
         return False
 
     def durations_ms(self):
@@ -291,18 +352,7 @@ class Buffers:
 
     def schedule_views(self) -> dict:
         """int32 views of the schedule table's parts (for inspection and tests)."""
-        L = schedule_layout_query(self.desc)
-        d = self.desc
-        s = self.sched
-
-        def iv(off, n):
-            return s[off: off + 4 * n].view(torch.int32)
-
-        return dict(counts=iv(L["counts"], d.E), offsets=iv(L["offsets"], d.E + 1),
-                    tile_start=iv(L["tile_start"], d.E + 1), num_tiles=iv(L["num_tiles"], 1),
-                    perm=iv(L["perm"], d.R), inv=iv(L["inv"], d.R),
-                    tiles=iv(L["tiles"], 4 * L["max_tiles"]).view(-1, 4), tile_m=L["tile_m"],
-                    max_tiles=L["max_tiles"])
+        return schedule_views(self.desc, self.sched)
 
     def saved_views(self) -> dict:
         """a, u [R, I] and h [R, I] in routed-row order (views into `saved`)."""

@@ -125,11 +125,14 @@ def forward_mx(x, weights, idx, gate, E: int, I: int, experts=None) -> dict:
     return dict(a=a_s, u=u_s, h=h_s, p=p, y=bf16_round(y))
 
 
-def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True, experts=None) -> dict:
+def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True, experts=None,
+                wfmt: str = "bf16") -> dict:
     """Gradients with MXFP8 expert GEMMs. `segments[e]` lists the lengths of expert e's
     row segments in slot order, token blocks restarting at each (default: one segment,
     the expert's rows of the whole step). ``experts`` restricts the work to a subset of
-    experts: only their d-gates, dGU, partial rows and weight gradients are formed."""
+    experts: only their d-gates, dGU, partial rows and weight gradients are formed.
+    ``wfmt`` is the storage format of dW1, dW2, dWr ('bf16', or 'f32' for weight
+    gradients kept in fp32); every other stored value is bf16."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     g = np.asarray(gate, np.float64)
@@ -162,8 +165,8 @@ def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, route
         q[s] = bf16_round(mx(G) @ mx(W1, axis=0))        # W1^T rows along 2I
         seg = [s.size] if segments is None else segments[e]
         dO = bf16_round(gf[s][:, None] * dy[t])
-        dw2[e] = bf16_round(mx_token_blocks(dO, seg).T @ mx_token_blocks(hh, seg))
-        dw1[e] = bf16_round(mx_token_blocks(G, seg).T @ mx_token_blocks(x[t], seg))
+        dw2[e] = round_to(mx_token_blocks(dO, seg).T @ mx_token_blocks(hh, seg), wfmt)
+        dw1[e] = round_to(mx_token_blocks(G, seg).T @ mx_token_blocks(x[t], seg), wfmt)
     if experts is not None:
         return dict(dgate=gp.reshape(T, k), dgu=dgu, dw1=dw1, dw2=dw2, q=q)
     gpk = gp.reshape(T, k)
@@ -184,6 +187,6 @@ def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, route
         for e, s in enumerate(by_e):
             if s.size:
                 dwr[e] = dzf[s] @ x[s // k]
-        out["dwr"] = bf16_round(dwr)
+        out["dwr"] = round_to(dwr, wfmt)
     out["dx"] = bf16_round(acc)
     return out

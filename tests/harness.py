@@ -59,6 +59,7 @@ def run_gpu(case: Case, backward=True, tile_m=0, grid=0, router_grad=True, wgrad
         mok.moe_backward(d, buf.sched, x, buf.idx, buf.gate, w1, w2, wr if router_grad else None, buf.saved, dy,
                          buf.dx, buf.dw1, buf.dw2, buf.dgate, buf.dwr if router_grad else None, buf.bwd_ws)
     torch.cuda.synchronize()
+    mok.check_schedule(d, buf.sched, "layer step")
     sv = buf.schedule_views()
     out.update(idx=buf.idx.cpu().numpy(), gate=buf.gate.cpu().numpy(), y=buf.y.cpu(),
                counts=sv["counts"].cpu().numpy(), offsets=sv["offsets"].cpu().numpy(),

@@ -35,12 +35,14 @@ def test_library_exports_every_declared_symbol(mok):
     for n in _declared():
         assert hasattr(lib, n), n
     assert set(_declared()) == set(mok.EXPORTS)
-    assert mok.version() == 201
+    assert mok.version() == 300
 
 
 def test_status_strings(mok):
-    for st in range(6):
+    for st in range(8):
         assert mok._lib.mok_status_string(st)
+    assert mok._lib.mok_status_string(6) != mok._lib.mok_status_string(99)
+    assert mok._lib.mok_status_string(7) != mok._lib.mok_status_string(99)
 
 
 def _d(mok, **kw):
@@ -103,9 +105,9 @@ def test_null_and_alignment_rejected_before_launch(mok):
                        ctypes.c_void_p(4096), None, None)
     assert st == 2
     # NULL schedule / weights struct
-    st = lib.mok_schedule_build(ctypes.byref(c), ctypes.c_void_p(4096), None, None)
+    st = lib.mok_schedule_build(ctypes.byref(c), ctypes.c_void_p(4096), None, 1 << 30, None)
     assert st == 1
-    st = lib.mok_moe_forward(ctypes.byref(c), ctypes.c_void_p(4096), None, None, None, None, None, None, None)
+    st = lib.mok_moe_forward(ctypes.byref(c), ctypes.c_void_p(4096), None, None, None, None, None, 0, None, 0, None)
     assert st == 1
     # MXFP8: weights_quantize needs gemm = MXFP8 and every output pointer
     q = mok._MxWeights(*([4096] * 8))
@@ -123,6 +125,52 @@ def test_null_and_alignment_rejected_before_launch(mok):
     assert st == 2
     # MXFP8 forward without the quantised weights
     w = mok._Weights(4096, 4096, None)
+    big = 1 << 40
     st = lib.mok_moe_forward(ctypes.byref(cm), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
-                             ctypes.byref(w), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None)
+                             ctypes.byref(w), ctypes.c_void_p(4096), ctypes.c_void_p(4096), big, ctypes.c_void_p(4096),
+                             big, None)
     assert st in (1, 5)
+
+
+def test_undersized_buffers_rejected_before_launch(mok):
+    """Each caller buffer is compared with mok_workspace_query's size before the device is
+    touched: one byte short gives MOK_ERR_WORKSPACE (no GPU needed), enough gives another
+    status (here MOK_ERR_HIP or a later check, since there is no device)."""
+    lib = mok._lib
+    P = ctypes.c_void_p
+    for kw in (dict(), dict(gemm=mok.MXFP8, mb_count=4, ring=2), dict(act=mok.F32)):
+        d = _d(mok, T=256, H=256, E=8, k=2, I=128, **kw)
+        c = d.c()
+        s = mok.workspace_query(d)
+        w = mok._Weights(4096, 4096, None)
+        st = lib.mok_schedule_build(ctypes.byref(c), P(4096), P(4096), s["sched"] - 1, None)
+        assert st == mok.ERR_WORKSPACE
+        st = lib.mok_schedule_build(ctypes.byref(c), P(4096), P(4096), s["sched"], None)
+        assert st != mok.ERR_WORKSPACE
+        for saved, ws in ((s["saved"] - 1, s["fwd_ws"]), (s["saved"], s["fwd_ws"] - 1)):
+            st = lib.mok_moe_forward(ctypes.byref(c), P(4096), P(4096), P(4096), ctypes.byref(w), P(4096), P(4096),
+                                     saved, P(4096), ws, None)
+            assert st == mok.ERR_WORKSPACE, (kw, saved, ws)
+        st = lib.mok_moe_forward(ctypes.byref(c), P(4096), P(4096), P(4096), ctypes.byref(w), P(4096), P(4096),
+                                 s["saved"], P(4096), s["fwd_ws"], None)
+        assert st != mok.ERR_WORKSPACE
+        for saved, ws in ((s["saved"] - 1, s["bwd_ws"]), (s["saved"], s["bwd_ws"] - 1)):
+            st = lib.mok_moe_backward(ctypes.byref(c), P(4096), P(4096), P(4096), P(4096), ctypes.byref(w), None,
+                                      P(4096), saved, P(4096), P(4096), P(4096), P(4096), P(4096), None, P(4096), ws,
+                                      None)
+            assert st == mok.ERR_WORKSPACE, (kw, saved, ws)
+
+
+def test_trace_binding_checks(mok):
+    """mok_trace_bind validates the caller-owned trace and unbinds with NULL."""
+    lib = mok._lib
+    t = mok._Trace()
+    assert lib.mok_trace_bind(ctypes.byref(t)) == 1          # NULL filter / events
+    ev = (ctypes.c_void_p * 2)()
+    t.filter = b"fc1"
+    t.events = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    t.capacity = mok.TRACE_MAX + 1
+    assert lib.mok_trace_bind(ctypes.byref(t)) == 3
+    t.capacity = 1
+    assert lib.mok_trace_bind(ctypes.byref(t)) == 0
+    assert lib.mok_trace_bind(None) == 0

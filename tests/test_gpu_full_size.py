@@ -3,9 +3,13 @@ launch configuration bench.py times (automatic tile height and grid).
 
 * routing for all tokens: logits, indices, counts, offsets, permutation, inverse and the
   tile table bit-exact against the oracle's router;
-* sampled tokens: y, saved a/u/h rows, dX and d-gate rows computed one token at a time by
-  the oracle, within the bf16 tolerance;
-* sampled experts: the whole dW1[e] and dW2[e] from the oracle over all of e's rows;
+* sampled tokens: y, saved a/u/h rows, dX and d-gate rows computed by the oracle over a
+  token subset, within the bf16 tolerance;
+* dWr[e] of the least-loaded expert that has rows: the token subset holds every token
+  routed to it, so the oracle forms the d-gates of all their slots (every expert they
+  touch) and dWr[e] over all of e's rows;
+* sampled experts (two random ones, and the most loaded one): the whole dW1[e] and dW2[e]
+  from the oracle over all of e's rows;
 * reproducibility: a second step gives bit-identical outputs.
 A second case uses the streamed workload's inputs and Zipf router bias (hottest expert
 about 8x the mean, 48 experts with no tokens) at the same shape, with bf16 GEMMs over the
@@ -48,8 +52,11 @@ def _run(w):
     sc = orc.schedule(idx, w.E, 128)
     tok = np.sort(rng.choice(w.T, N_TOK, replace=False))
     busy = np.nonzero(sc["counts"])[0]
-    exps = sorted(rng.choice(busy, N_EXP, replace=False).tolist())
-    need = set(idx[tok].ravel().tolist()) | set(exps)
+    exps = sorted(set(rng.choice(busy, N_EXP, replace=False).tolist()) | {int(np.argmax(sc["counts"]))})
+    e_wr = int(busy[np.argmin(sc["counts"][busy])])           # least-loaded expert with rows: its dWr row
+    tok_wr = np.nonzero((idx == e_wr).any(axis=1))[0]
+    sub = np.union1d(tok, tok_wr)                              # token subset of the oracle's step
+    need = set(idx[sub].ravel().tolist()) | set(exps)
 
     w1 = torch.empty(w.E, 2 * w.I, w.H, dtype=torch.bfloat16, device=dev)
     w2 = torch.empty(w.E, w.H, w.I, dtype=torch.bfloat16, device=dev)
@@ -75,6 +82,7 @@ def _run(w):
         mok.moe_backward(d, buf.sched, x, buf.idx, buf.gate, w1, w2, wr, buf.saved, dy, buf.dx, buf.dw1,
                          buf.dw2, buf.dgate, buf.dwr, buf.bwd_ws)
         torch.cuda.synchronize()
+        mok.check_schedule(d, buf.sched, "layer step")
 
     step()
     sv = buf.schedule_views()
@@ -92,21 +100,24 @@ def _run(w):
     assert nt == len(sc_g["tiles"])
     np.testing.assert_array_equal(sv["tiles"].cpu().numpy()[:nt, :3], sc_g["tiles"])
 
-    # ---- sampled tokens: forward and backward rows, one token at a time
+    # ---- token subset: sampled tokens' rows, and dWr of e_wr (all of its tokens are in it)
     W = _Weights(kept)
-    xs = x_cpu.float().numpy()[tok]
-    fwd = orc.forward(xs, W, idx[tok], g[tok], "bf16", w.E, w.I)
-    bwd = orc.backward(xs, W, wr_cpu.float().numpy(), idx[tok], g[tok], fwd, dy_cpu.float().numpy()[tok], "bf16",
+    xs = x_cpu.float().numpy()[sub]
+    fwd = orc.forward(xs, W, idx[sub], g[sub], "bf16", w.E, w.I)
+    bwd = orc.backward(xs, W, wr_cpu.float().numpy(), idx[sub], g[sub], fwd, dy_cpu.float().numpy()[sub], "bf16",
                        w.I)
+    pos = np.searchsorted(sub, tok)                            # sampled tokens inside the subset
     saved = buf.saved_views()
     rows = sc_g["inv"][(tok[:, None] * w.k + np.arange(w.k)[None, :]).ravel()]
+    srow = (pos[:, None] * w.k + np.arange(w.k)[None, :]).ravel()
     errs = {
-        "y": rel_fro(np64(buf.y[tok]), fwd["y"]),
-        "a": rel_fro(np64(saved["a"][rows]), fwd["a"]),
-        "u": rel_fro(np64(saved["u"][rows]), fwd["u"]),
-        "h": rel_fro(np64(saved["h"][rows]), fwd["h"]),
-        "dx": rel_fro(np64(buf.dx[tok]), bwd["dx"]),
-        "dgate": rel_fro(buf.dgate[tok].cpu().numpy(), bwd["dgate"]),
+        "y": rel_fro(np64(buf.y[tok]), fwd["y"][pos]),
+        "a": rel_fro(np64(saved["a"][rows]), fwd["a"][srow]),
+        "u": rel_fro(np64(saved["u"][rows]), fwd["u"][srow]),
+        "h": rel_fro(np64(saved["h"][rows]), fwd["h"][srow]),
+        "dx": rel_fro(np64(buf.dx[tok]), bwd["dx"][pos]),
+        "dgate": rel_fro(buf.dgate[tok].cpu().numpy(), bwd["dgate"][pos]),
+        "dwr[%d]" % e_wr: rel_fro(np64(buf.dwr[e_wr]), bwd["dwr"][e_wr]),
     }
 
     # ---- sampled experts: whole dW1[e], dW2[e] over all of e's rows (all tokens)
@@ -141,10 +152,13 @@ def test_kimi_k2_full_size_zipf_imbalanced():
 def test_kimi_k2_mxfp8_streamed_full_size():
     """The streamed MXFP8 workload at full size, in the launch configuration bench.py times:
     8 micro-batches of 2048 tokens, 2-slot ring, Zipf routing, weight gradients deferred to
-    the last backward call. Routing of all 16384 tokens bit-exact; one sampled token's y,
-    dX and d-gates, and the whole dW1[e], dW2[e] of two of its experts (over all of their
-    rows of the step) against the oracle's MXFP8 step within 2e-2; a second step gives
-    the same bits."""
+    the last backward call. Routing of all 16384 tokens bit-exact, and each micro-batch's
+    schedule (counts, offsets, permutation, inverse, tiles) bit-exact; against the oracle's
+    MXFP8 step within 2e-2: three sampled tokens' y, dX and d-gates, the dWr row of the
+    least-loaded expert with rows (the oracle's token subset holds all of its tokens), and
+    the whole dW1[e], dW2[e] of the most loaded expert (about 8x the mean: the long
+    weight-gradient K segment) and of the least-loaded expert of a sampled token, over all
+    of their rows of the step; a second step gives the same bits."""
     from mixture_experts_layer_stable_amd import mok
     w = inputs.WORKLOADS["kimi_k2_mxfp8_stream"]
     M = w.micro_batches
@@ -154,11 +168,16 @@ def test_kimi_k2_mxfp8_streamed_full_size():
     b = inputs.make_bias(w)
     z, idx, g = orc.route(x_cpu.float().numpy(), wr_cpu.float().numpy(), w.k, b.numpy())
     counts = np.bincount(idx.ravel(), minlength=w.E)
-    tok = np.array([int(rng.integers(w.T))])
-    exps = sorted(idx[tok[0]].tolist(), key=lambda e: counts[e])[:2]
-    need = set(idx[tok].ravel().tolist())
-    print("case mxfp8 stream T=%d M=%d token %d experts %s rows %s" % (w.T, M, tok[0], exps,
-          [int(counts[e]) for e in exps]), flush=True)
+    tok = np.sort(rng.choice(w.T, 3, replace=False))
+    busy = np.nonzero(counts)[0]
+    e_wr = int(busy[np.argmin(counts[busy])])
+    tok_wr = np.nonzero((idx == e_wr).any(axis=1))[0]
+    sub = np.union1d(tok, tok_wr)
+    exps = sorted({int(np.argmax(counts)), min(idx[tok[0]].tolist(), key=lambda e: counts[e])})
+    need = set(idx[sub].ravel().tolist()) | set(exps)
+    print("case mxfp8 stream T=%d M=%d tokens %s experts %s rows %s dWr expert %d (%d rows), %d experts in the "
+          "token subset" % (w.T, M, tok.tolist(), exps, [int(counts[e]) for e in exps], e_wr, counts[e_wr],
+                            len(need)), flush=True)
 
     d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, mb_count=M, ring=2)
     q = mok.MxWeights(d, dev)
@@ -182,13 +201,25 @@ def test_kimi_k2_mxfp8_streamed_full_size():
 
     np.testing.assert_array_equal(st.idx.cpu().numpy(), idx)
     assert rel_fro(st.gate.cpu().numpy(), g) <= 1e-6
+    Tm = w.T // M
+    for m in range(M):
+        sv = mok.schedule_views(d, st.sched[m])
+        assert sv["status"] == 0
+        scm = orc.schedule(idx[m * Tm:(m + 1) * Tm], w.E, sv["tile_m"])
+        for key in ("counts", "offsets", "perm", "inv"):
+            np.testing.assert_array_equal(sv[key].cpu().numpy(), scm[key], err_msg="micro-batch %d %s" % (m, key))
+        nt = int(sv["num_tiles"].cpu()[0])
+        assert nt == len(scm["tiles"])
+        np.testing.assert_array_equal(sv["tiles"].cpu().numpy()[:nt, :3], scm["tiles"])
 
     W = _Weights(kept)
     xs, dys, wrs = x_cpu.float().numpy(), dy_cpu.float().numpy(), wr_cpu.float().numpy()
-    f = orc.mx.forward_mx(xs[tok], W, idx[tok], g[tok], w.E, w.I)
-    bw = orc.mx.backward_mx(xs[tok], W, wrs, idx[tok], g[tok], f, dys[tok], w.I)
-    errs = {"y": rel_fro(np64(st.y[tok]), f["y"]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"]),
-            "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"])}
+    f = orc.mx.forward_mx(xs[sub], W, idx[sub], g[sub], w.E, w.I)
+    bw = orc.mx.backward_mx(xs[sub], W, wrs, idx[sub], g[sub], f, dys[sub], w.I)
+    pos = np.searchsorted(sub, tok)
+    errs = {"y": rel_fro(np64(st.y[tok]), f["y"][pos]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"][pos]),
+            "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"][pos]),
+            "dwr[%d]" % e_wr: rel_fro(np64(st.dwr[e_wr]), bw["dwr"][e_wr])}
     for e in exps:
         fe = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, experts=[e])
         be = orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e])

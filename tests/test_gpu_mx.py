@@ -83,10 +83,11 @@ def _case(w):
     return x, dy, wr, b, w1, w2
 
 
-def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True):
+def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True, wgrad_f32=False):
     mok = _mok()
-    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m)
-    buf = mok.Buffers(d, DEV)
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m,
+                 flags=mok.FLAG_WGRAD_F32 if wgrad_f32 else 0)
+    buf = mok.Buffers(d, DEV, wgrad_f32=wgrad_f32)
     q = mok.MxWeights(d, DEV)
     w1d, w2d = w1.to(DEV), w2.to(DEV)
     mok.weights_quantize(d, w1d, w2d, q)
@@ -94,6 +95,7 @@ def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True):
     bd = None if b is None else b.to(DEV)
     mok.step(d, buf, xd, wrd, bd, None, None, dyd, router_grad=router_grad, mxw=q)
     torch.cuda.synchronize()
+    mok.check_schedule(d, buf.sched, "MXFP8 step")
     out = dict(idx=buf.idx.cpu().numpy(), gate=buf.gate.cpu(), y=buf.y.cpu(), dx=buf.dx.cpu(),
                dgate=buf.dgate.cpu(), dw1=buf.dw1.cpu(), dw2=buf.dw2.cpu(), perm=buf.schedule_views()["perm"].cpu())
     if router_grad:
@@ -116,12 +118,12 @@ def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0):
                 dw1=st.dw1.cpu(), dw2=st.dw2.cpu(), dwr=st.dwr.cpu())
 
 
-def _oracle(w, x, dy, wr, b, w1, w2):
+def _oracle(w, x, dy, wr, b, w1, w2, wfmt="bf16"):
     xs, dys, wrs = x.float().numpy(), dy.float().numpy(), wr.float().numpy()
     z, idx, g = orc.route(xs, wrs, w.k, None if b is None else b.numpy())
     W = orc.DenseWeights(w1.float().numpy(), w2.float().numpy())
     f = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I)
-    bw = orc.mx.backward_mx(xs, W, wrs, idx, g, f, dys, w.I)
+    bw = orc.mx.backward_mx(xs, W, wrs, idx, g, f, dys, w.I, wfmt=wfmt)
     return idx, g, f, bw
 
 
@@ -259,3 +261,140 @@ def test_mx_streamed_three_slots_odd_count():
         a, c = st[n], whole[n]
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            c.view(torch.int16) if c.dtype == torch.bfloat16 else c), n
+
+
+def test_mx_wgrad_f32():
+    """MXFP8 with MOK_FLAG_WGRAD_F32: fp32 weight gradients (one output tile per workgroup) and
+    the fp32 dWr sums, against the oracle's MXFP8 step with dW kept in fp32."""
+    w = inputs.replace(MX_CASES["imbalanced"], T=512, H=256, E=8, k=2, I=256)
+    x, dy, wr, b, w1, w2 = _case(w)
+    g = _run_whole(w, x, dy, wr, b, w1, w2, wgrad_f32=True)
+    assert g["dw1"].dtype == torch.float32 and g["dwr"].dtype == torch.float32
+    idx, gate, f, bw = _oracle(w, x, dy, wr, b, w1, w2, wfmt="f32")
+    np.testing.assert_array_equal(g["idx"], idx)
+    errs = {"dw1": rel_fro(np64(g["dw1"]), np.stack([bw["dw1"][e] for e in range(w.E)])),
+            "dw2": rel_fro(np64(g["dw2"]), np.stack([bw["dw2"][e] for e in range(w.E)])),
+            "dwr": rel_fro(np64(g["dwr"]), bw["dwr"]), "dx": rel_fro(np64(g["dx"]), bw["dx"])}
+    print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_MX, (k, v)
+
+
+# ---------------------------------------------------------------------------------------
+# Bit-exact checks of the quantisers inside the step: the activation row quantisers (x, dY),
+# the fc1 / dh epilogue quantisers (h, dGU) and the flush's token-axis quantisers (dO, h,
+# dGU, x over each expert's rows of the step). Expected bytes are the oracle quantiser's
+# encoding of the oracle's own bf16 values. Where a value is the result of a GEMM (h, dGU)
+# or of a product with the fp32 gate (dO), the GPU's bf16 value can differ from the
+# oracle's by one rounding step; a 32-element block is compared only where the GPU's stored
+# bf16 inputs of that block equal the oracle's (the GPU values only select blocks, they are
+# never an input of the expected bytes), and at least 90 % of the blocks must be compared.
+
+def _kmaj(s_u8: torch.Tensor, rows: int, kb: int) -> np.ndarray:
+    """K-tile-major scale bytes [kb/4][rows][4] -> exponents [rows][kb]."""
+    a = s_u8.cpu().numpy().astype(np.int64)[: kb * rows].reshape(kb // 4, rows, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2)).reshape(rows, kb) - 127
+
+
+def _bf16_rows(buf: torch.Tensor, off: int, rows: int, cols: int) -> np.ndarray:
+    return buf[off: off + 2 * rows * cols].view(torch.bfloat16).view(rows, cols).double().numpy()
+
+
+def _compare_blocks(name, got_el, got_s, ref_vals, gate_vals, axis_rows=False):
+    """got_el/got_s: decoded GPU elements and scale exponents; ref_vals: the oracle's bf16
+    values (blocks of 32 along the last axis, or along axis 0 when axis_rows); gate_vals:
+    the GPU's stored bf16 values of the same elements."""
+    if axis_rows:
+        got_el, ref_vals, gate_vals = got_el.T, ref_vals.T, gate_vals.T
+        got_s = got_s.T
+    el, s = orc.mx.mx_quantize(ref_vals, -1)
+    nb = ref_vals.shape[-1] // 32
+    same = np.all((ref_vals == gate_vals).reshape(ref_vals.shape[:-1] + (nb, 32)), axis=-1)
+    frac = same.mean()
+    assert frac >= 0.9, (name, "blocks comparable", frac)
+    np.testing.assert_array_equal(got_s[same], s[same], err_msg=name + " scales")
+    bel = got_el.reshape(el.shape[:-1] + (nb, 32))[same]
+    np.testing.assert_array_equal(bel, el.reshape(el.shape[:-1] + (nb, 32))[same], err_msg=name + " elements")
+    return frac
+
+
+def test_mx_step_quantisers_bit_exact():
+    mok = _mok()
+    w = inputs.replace(MX_CASES["imbalanced"], T=512, H=256, E=8, k=2, I=256)
+    M = 2
+    x, dy, wr, b, w1, w2 = _case(w)
+    Tm = w.T // M
+    d = mok.Desc(Tm, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, mb_count=M, ring=M)
+    st = mok.StreamedStep(d, DEV)
+    q = mok.MxWeights(d, DEV)
+    mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
+    st.run(x.to(DEV), wr.to(DEV), b.to(DEV), q, dy.to(DEV))
+    torch.cuda.synchronize()
+    L = mok.mx_layout_query(d)
+    idx, g, f, bw = _oracle(w, x, dy, wr, b, w1, w2)
+    np.testing.assert_array_equal(st.idx.cpu().numpy(), idx)
+    H, I, k, E = w.H, w.I, w.k, w.E
+    R = Tm * k
+    xs, dys = x.double().numpy(), dy.double().numpy()
+    fw, bwk = st.fwd_ws, st.bwd_ws
+    fracs = {}
+    rows_e = {e: [] for e in range(E)}           # (micro-batch, routed row, global slot) per expert
+    for m in range(M):
+        sc = orc.schedule(idx[m * Tm:(m + 1) * Tm], E, 32)
+        gslot = m * R + sc["perm"]                # routed row -> global flat slot
+        fo, bo = m * L["fwd_slot"], m * L["bwd_slot"]
+        # x and dY rows (inputs: every block compared)
+        xq = _decode_e4m3(fw[fo + L["xq"]: fo + L["xq"] + Tm * H]).reshape(Tm, H)
+        el, s = orc.mx.mx_quantize(xs[m * Tm:(m + 1) * Tm], -1)
+        np.testing.assert_array_equal(xq, el)
+        np.testing.assert_array_equal(_kmaj(fw[fo + L["xs"]:], Tm, H // 32), s)
+        dq = _decode_e4m3(bwk[bo + L["dyq"]: bo + L["dyq"] + Tm * H]).reshape(Tm, H)
+        el, s = orc.mx.mx_quantize(dys[m * Tm:(m + 1) * Tm], -1)
+        np.testing.assert_array_equal(dq, el)
+        np.testing.assert_array_equal(_kmaj(bwk[bo + L["dys"]:], Tm, H // 32), s)
+        # fc1 epilogue: h rows (routed order) along I
+        hg = mok.saved_layout_query(d)["h_offset"]
+        h_gpu = _bf16_rows(st.saved[m], hg, R, I)
+        hq = _decode_e4m3(fw[fo + L["hq"]: fo + L["hq"] + R * I]).reshape(R, I)
+        fracs["h%d" % m] = _compare_blocks("hq", hq, _kmaj(fw[fo + L["hs"]:], R, I // 32), f["h"][gslot], h_gpu)
+        # dh epilogue: dGU rows along 2I (the GPU's bf16 dGU rows are in the stash)
+        dgu_gpu = _bf16_rows(bwk, L["st_dgu"] + 2 * m * R * 2 * I, R, 2 * I)
+        gq = _decode_e4m3(bwk[bo + L["dguq"]: bo + L["dguq"] + R * 2 * I]).reshape(R, 2 * I)
+        fracs["dgu%d" % m] = _compare_blocks("dguq", gq, _kmaj(bwk[bo + L["dgus"]:], R, 2 * I // 32),
+                                             bw["dgu"][gslot], dgu_gpu)
+        for e in range(E):
+            for r in range(sc["offsets"][e], sc["offsets"][e + 1]):
+                rows_e[e].append((m * R + r, gslot[r]))
+    # flush: token-axis operands over each expert's rows of the whole step, 128-padded segments
+    K = L["kmax"]
+    pofs = bwk[L["pofs"]: L["pofs"] + 4 * (E + 1)].view(torch.int32).cpu().numpy()
+    gflat = g.ravel()
+    ops = {  # name: (q, s, F, stash offset, oracle rows by global slot)
+        "dO": ("dot", "dots", H, L["st_dos"], lambda s_: orc.bf16_round(gflat[s_][:, None] * dys[s_ // k])),
+        "h": ("ht", "hts", I, L["st_h"], lambda s_: f["h"][s_]),
+        "dGU": ("dgut", "dguts", 2 * I, L["st_dgu"], lambda s_: bw["dgu"][s_]),
+        "x": ("xt", "xts", H, L["st_xs"], lambda s_: xs[s_ // k]),
+    }
+    for name, (qn, sn, F, so, ref_fn) in ops.items():
+        qall = _decode_e4m3(bwk[L[qn]: L[qn] + F * K]).reshape(F, K)
+        sall = _kmaj(bwk[L[sn]:], F, K // 32)                   # [F][K/32]
+        stash = _bf16_rows(bwk, so, M * R, F)
+        tot = 0
+        for e in range(E):
+            n = len(rows_e[e])
+            pad = pofs[e + 1] - pofs[e]
+            assert pad == -(-n // 128) * 128, (e, n, pad)
+            if n == 0:
+                continue
+            st_rows = np.array([r for r, _ in rows_e[e]])
+            slots = np.array([s_ for _, s_ in rows_e[e]])
+            ref = np.zeros((pad, F))
+            gate_v = np.zeros((pad, F))
+            ref[:n] = ref_fn(slots)
+            gate_v[:n] = stash[st_rows]
+            p0 = pofs[e]
+            fr = _compare_blocks(name + "[%d]" % e, qall[:, p0:p0 + pad].T, sall[:, p0 // 32:(p0 + pad) // 32].T,
+                                 ref, gate_v, axis_rows=True)
+            tot += fr
+        fracs[name] = tot
+    print("blocks compared:", {k_: "%.3f" % v for k_, v in fracs.items()}, flush=True)

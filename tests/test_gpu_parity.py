@@ -114,11 +114,12 @@ def test_route_token_group_sizes(T):
 
 @pytest.mark.parametrize("T,E,k,H,I", [(77, 5, 2, 128, 128), (130, 100, 3, 256, 384), (40, 600, 4, 128, 128),
                                        (33, 8, 8, 128, 256), (50, 1, 1, 128, 128), (96, 40, 3, 384, 256),
-                                       (64, 64, 2, 2048, 128)])
+                                       (64, 64, 2, 2048, 128), (256, 16, 2, 4096, 128)])
 def test_ragged_and_odd_shapes(T, E, k, H, I):
     """Token counts that are not tile multiples, E not a multiple of 64, E > 512, k = E, E = 1;
     H = 384 (six 64-h chunks: a partial group of the small-batch router's 4-chunk Wr
-    prefetch) and H = 2048 (the largest H whose x rows that router stages whole)."""
+    prefetch), H = 2048 (the largest H whose x rows that router stages whole) and H = 4096
+    (above 2048 the router backward's dWr uses its 32-lane x 8-vector shape)."""
     w = _w("small_bf16", T=T, E=E, k=k, H=H, I=I)
     print("case", w, flush=True)
     _full(w)
@@ -179,9 +180,11 @@ def test_no_router_backward():
     _check_backward(w, g, o, TOL["bf16"], router=False)
 
 
-def test_wgrad_f32_flag():
-    """MOK_FLAG_WGRAD_F32 writes dW1/dW2/dWr in fp32 (compared to the fp64 oracle rounded to fp32)."""
-    w = _w("small_bf16", T=128, E=8, k=2, H=128, I=128)
+@pytest.mark.parametrize("H,I", [(128, 128), (256, 256)])
+def test_wgrad_f32_flag(H, I):
+    """MOK_FLAG_WGRAD_F32 writes dW1/dW2/dWr in fp32 (compared to the fp64 oracle rounded to fp32);
+    H = I = 256 takes the 256 x 256 fp32-output weight-gradient tiles."""
+    w = _w("small_bf16", T=128, E=8, k=2, H=H, I=I)
     case = Case(w)
     g = run_gpu(case, wgrad_f32=True)
     assert g["dw1"].dtype == torch.float32
@@ -206,3 +209,41 @@ def test_bit_reproducible_across_runs_tiles_and_grids(name):
         for key in ("y", "a", "u", "h", "dx", "dw1", "dw2", "dwr"):
             assert torch.equal(g[key].view(torch.int16) if g[key].dtype == torch.bfloat16 else g[key],
                                ref[key].view(torch.int16) if ref[key].dtype == torch.bfloat16 else ref[key]), (kw, key)
+
+
+def test_schedule_built_for_another_descriptor_is_rejected():
+    """A schedule built for one descriptor and handed to forward/backward with another: every
+    kernel checks the header's descriptor hash first, so nothing is written (outputs keep
+    their sentinel) and the header's status word reads MOK_ERR_SCHEDULE_MISMATCH. Building
+    the schedule for the right descriptor clears it."""
+    from mixture_experts_layer_stable_amd import mok
+    w = _w("small_bf16", T=96, E=8, k=2, H=128, I=128)
+    case = Case(w)
+    dev = "cuda"
+    d_b = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16)
+    for d_a in (mok.Desc(w.T, w.H, 12, w.k, w.I, act=mok.BF16), mok.Desc(64, w.H, w.E, w.k, w.I, act=mok.BF16),
+                mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, tile_m=64)):
+        print("case schedule for", d_a, flush=True)
+        buf = mok.Buffers(d_b, dev)
+        nb = max(mok.workspace_query(d_a)["sched"], mok.workspace_query(d_b)["sched"])
+        buf.sched = torch.empty(nb, dtype=torch.uint8, device=dev)
+        x, wr = case.x.to(dev), case.wr.to(dev)
+        w1, w2, dy = case.w1.to(dev), case.w2.to(dev), case.dy.to(dev)
+        mok.route(d_b, x, wr, None, buf.idx, buf.gate)
+        idx_a = torch.zeros(d_a.T, d_a.k, dtype=torch.int32, device=dev)
+        mok.schedule_build(d_a, idx_a, buf.sched)       # same buffer, other descriptor
+        for t in (buf.y, buf.dx, buf.dw1, buf.dw2, buf.dwr):
+            t.fill_(7.0)
+        buf.dgate.fill_(7.0)
+        mok.moe_forward(d_b, buf.sched, x, buf.gate, w1, w2, buf.y, buf.saved, buf.fwd_ws)
+        mok.moe_backward(d_b, buf.sched, x, buf.idx, buf.gate, w1, w2, wr, buf.saved, dy, buf.dx, buf.dw1, buf.dw2,
+                         buf.dgate, buf.dwr, buf.bwd_ws)
+        torch.cuda.synchronize()
+        assert mok.schedule_status(d_b, buf.sched) == mok.ERR_SCHEDULE_MISMATCH
+        with pytest.raises(mok.MokError):
+            mok.check_schedule(d_b, buf.sched)
+        for t in (buf.y, buf.dx, buf.dw1, buf.dw2, buf.dwr, buf.dgate):
+            assert torch.all(t == 7.0)
+        mok.schedule_build(d_b, buf.idx, buf.sched)
+        torch.cuda.synchronize()
+        assert mok.schedule_status(d_b, buf.sched) == 0
