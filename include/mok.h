@@ -264,6 +264,22 @@ mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const 
                            void* y, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mok_moe_forward_noalloc -- mok_moe_forward (same kernels, same results) for callers that
+ * cannot allocate device memory (code under stream capture, tight serving loops): the
+ * forward workspace is a library-owned device array of MOK_NOALLOC_WS_BYTES (32 MiB) per
+ * GPU instead of a caller buffer, so no allocation happens in or for the call.  Returns
+ * MOK_ERR_WORKSPACE when mok_sizes.fwd_ws of d exceeds it (e.g. the 2048-token bf16 layer
+ * needs 8 MiB and fits; a 16384-token Kimi-K2-shaped one does not).  The array holds only
+ * values a call writes before it reads them (nothing must start at zero).  Every call on
+ * one GPU shares that GPU's array: calls that may overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued; calls ordered on one stream are
+ * safe.  sched, x, gate, w, y, saved, saved_bytes and stream as for mok_moe_forward.
+ */
+#define MOK_NOALLOC_WS_BYTES ((size_t)32 << 20)
+mok_status mok_moe_forward_noalloc(const mok_desc* d, void* sched, const void* x, const float* gate,
+                                   const mok_weights* w, void* y, void* saved, size_t saved_bytes, void* stream);
+
+/*
  * mok_moe_backward -- gradients of L = <dy, y>.
  *   pull reverse-combine: dy rows gathered through perm into the dH GEMM;
  *   dA = dy_t.W2[e]; the gate gradient g'_s = <dA, h> (= <dy_t, o_s>) is

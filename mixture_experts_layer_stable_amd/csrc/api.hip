@@ -245,6 +245,28 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
     if (!aligned16(p)) return MOK_ERR_ALIGN; \
   } while (0)
 
+// ---- workspace of mok_moe_forward_noalloc: a file-scope device array ----
+// In host code `scratch` only names the symbol; its device address (one per GPU, each GPU
+// holds its own copy until the process ends) comes from hipGetSymbolAddress, taken once
+// per device with that device current and cached here.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+mok_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOK_ERR_HIP;
+    cache[dev] = p;
+  }
+  *out = cache[dev];
+  return MOK_OK;
+}
+
 // Buffer sizes passed by the caller against what the descriptor needs.
 mok_status need(size_t have, size_t want) { return have >= want ? MOK_OK : MOK_ERR_WORKSPACE; }
 
@@ -495,6 +517,17 @@ mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const 
   MOK_LAUNCH("fc2", c.s, launch_fc2(c, sv + L.h, w->w2, ws));
   MOK_LAUNCH("combine", c.s, launch_combine(c, ws, gate, y));
   return MOK_OK;
+}
+
+mok_status mok_moe_forward_noalloc(const mok_desc* d, void* sched, const void* x, const float* gate,
+                                   const mok_weights* w, void* y, void* saved, size_t saved_bytes, void* stream) {
+  mok_sizes sz;
+  mok_status st = mok_workspace_query(d, &sz);
+  if (st != MOK_OK) return st;
+  if (sz.fwd_ws > kScratchBytes) return MOK_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != MOK_OK) return st;
+  return mok_moe_forward(d, sched, x, gate, w, y, saved, saved_bytes, ws, kScratchBytes, stream);
 }
 
 mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const int32_t* idx, const float* gate,

@@ -98,6 +98,7 @@ def _load():
         "mok_route": [D, P, P, P, P, P, P, P],
         "mok_schedule_build": [D, P, P, Z, P],
         "mok_moe_forward": [D, P, P, P, ctypes.POINTER(_Weights), P, P, Z, P, Z, P],
+        "mok_moe_forward_noalloc": [D, P, P, P, ctypes.POINTER(_Weights), P, P, Z, P],
         "mok_moe_backward": [D, P, P, P, P, ctypes.POINTER(_Weights), P, P, Z, P, P, P, P, P, P, P, Z, P],
         "mok_trace_bind": [ctypes.POINTER(_Trace)],
         "mok_weights_quantize": [D, P, P, ctypes.POINTER(_MxWeights), P],
@@ -116,8 +117,9 @@ def _load():
 _lib = _load()
 EXPORTS = ("mok_workspace_query", "mok_schedule_layout_query", "mok_saved_layout_query", "mok_mx_layout_query",
            "mok_route",
-           "mok_schedule_build", "mok_moe_forward", "mok_moe_backward", "mok_weights_quantize", "mok_status_string",
-           "mok_version", "mok_trace_bind")
+           "mok_schedule_build", "mok_moe_forward", "mok_moe_forward_noalloc", "mok_moe_backward",
+           "mok_weights_quantize", "mok_status_string", "mok_version", "mok_trace_bind")
+NOALLOC_WS_BYTES = 32 << 20
 
 
 @dataclass
@@ -272,6 +274,13 @@ def moe_forward(d: Desc, sched, x, gate, w1, w2, y, saved, ws, stream=None, mxw:
     w, _keep = _weights(w1, w2, mxw)
     _check(_lib.mok_moe_forward(ctypes.byref(d.c()), _p(sched), _p(x), _p(gate), ctypes.byref(w), _p(y), _p(saved),
                                 _nb(saved), _p(ws), _nb(ws), _stream(stream)), "mok_moe_forward")
+
+
+def moe_forward_noalloc(d: Desc, sched, x, gate, w1, w2, y, saved, stream=None, mxw: Optional[MxWeights] = None):
+    """mok_moe_forward_noalloc: the forward with the library's own device workspace."""
+    w, _keep = _weights(w1, w2, mxw)
+    _check(_lib.mok_moe_forward_noalloc(ctypes.byref(d.c()), _p(sched), _p(x), _p(gate), ctypes.byref(w), _p(y),
+                                        _p(saved), _nb(saved), _stream(stream)), "mok_moe_forward_noalloc")
 
 
 def moe_backward(d: Desc, sched, x, idx, gate, w1, w2, wr, saved, dy, dx, dw1, dw2, dgate, dwr, ws, stream=None,

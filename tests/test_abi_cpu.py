@@ -174,3 +174,15 @@ def test_trace_binding_checks(mok):
     t.capacity = 1
     assert lib.mok_trace_bind(ctypes.byref(t)) == 0
     assert lib.mok_trace_bind(None) == 0
+
+
+def test_noalloc_forward_refuses_oversized_workspace_before_launch(mok):
+    """mok_moe_forward_noalloc compares the descriptor's forward workspace with its 32 MiB
+    device array before touching the device (no GPU needed)."""
+    P = ctypes.c_void_p
+    d = _d(mok, T=16384, H=7168, E=384, k=8, I=2048)
+    assert mok.workspace_query(d)["fwd_ws"] > mok.NOALLOC_WS_BYTES
+    w = mok._Weights(4096, 4096, None)
+    st = mok._lib.mok_moe_forward_noalloc(ctypes.byref(d.c()), P(4096), P(4096), P(4096), ctypes.byref(w), P(4096),
+                                          P(4096), 1 << 40, None)
+    assert st == mok.ERR_WORKSPACE
