@@ -81,7 +81,7 @@ int choose_tile_m(int64_t R, int I, int cus) {
 
 struct Layout {
   int BM = 32, max_tiles = 0;
-  size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, sched;  // header at 0
+  size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, hist, sched;  // header at 0
   size_t au, h, saved;
   size_t fwd_part, fwd;
   size_t dgu, bpart, dgp, dz, xs, dos, bwd;
@@ -104,6 +104,7 @@ Layout layout_of(const mok_desc* d, int BM) {
   L.perm = o; o = up(o + 4 * (size_t)R);
   L.inv = o; o = up(o + 4 * (size_t)R);
   L.tiles = o; o = up(o + 16 * (size_t)std::max<int64_t>(worst_tiles, 1));
+  L.hist = o; o = up(o + 4 * (size_t)d->E * (size_t)((R + sched_block(R) - 1) / sched_block(R)));  // build scratch
   L.sched = o;
   o = 0;
   L.au = o; o = up(o + es * (size_t)R * 2 * d->I);
@@ -236,6 +237,7 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
   c->perm = (int32_t*)(sb + L.perm);
   c->inv = (int32_t*)(sb + L.inv);
   c->tiles = (int4*)(sb + L.tiles);
+  c->hist = (int32_t*)(sb + L.hist);
   return MOK_OK;
 }
 

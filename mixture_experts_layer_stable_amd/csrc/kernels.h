@@ -26,6 +26,7 @@ struct Ctx {
   int32_t* perm;
   int32_t* inv;
   int4* tiles;
+  int32_t* hist;   // schedule build scratch: per-(expert, slot block) counts, then bases
 };
 
 hipError_t launch_route(const Ctx& c, const void* x, const void* wr, const float* bias, int32_t* idx, float* gate,
@@ -88,6 +89,11 @@ hipError_t launch_dx_mx(const Ctx& c, const void* dguq, const void* dgus, const 
                         void* part);
 hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const void* as, const void* bq,
                         const void* bs, void* out, int M, int N, int64_t kld);
+
+// Slots per histogram / scatter block of the schedule build (1024 up to 65536 routed rows
+// so that a few thousand rows still spread over several workgroups, 4096 above); shared
+// by the schedule's scratch sizing and its launches.
+inline int sched_block(int64_t R) { return R <= 65536 ? 1024 : 4096; }
 
 // Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
 inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }

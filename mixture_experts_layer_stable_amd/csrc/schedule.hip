@@ -2,14 +2,20 @@
 // MoK mechanism": one schedule drives dispatch, combine, reverse-combine and
 // reverse-dispatch).
 //
-// A stable counting sort of the R = T*k flat slots by expert, done without
-// atomics so that it is exact and independent of scheduling:
-//   1. count:  one wave per expert scans idx and counts its slots;
-//   2. scan:   one workgroup forms exclusive offsets and per-expert tile starts
-//              and writes the tile list (expert, first row, rows);
-//   3. rank:   one wave per expert scans idx again in ascending slot order; a
-//              slot's row is offsets[e] + number of earlier slots of e
-//              (ballot + popcount), giving perm (row -> slot) and inv.
+// A stable counting sort of the R = T*k flat slots by expert, with work O(R + E)
+// and no atomics on global memory, so it is exact and independent of scheduling:
+//   1. hist:    block b (sched_block(R) consecutive slots) counts its slots per expert
+//               (integer LDS counters) -> hist[e][b];
+//   2. scan:    one workgroup sums each expert's block counts (counts), forms the
+//               exclusive offsets and per-expert tile starts, writes the tile list
+//               (expert, first row, rows) and turns hist[e][b] into the first row of
+//               expert e's slots from block b (offsets[e] + earlier blocks' counts);
+//   3. scatter: block b again; each of 16 waves takes 1/16 of its slots, its
+//               per-expert bases come from hist and the earlier waves' counts, and
+//               inside a group of 64 slots a lane's rank among equal experts is the
+//               number of lower lanes holding the same expert. Row of slot s =
+//               base + rank, so rows follow ascending slot order within each expert:
+//               perm (row -> slot) and inv.
 // The scan step also stamps the header (descriptor hash, tile height, tile
 // capacity, status MOK_OK) that the forward and backward kernels check.
 #include "kernels.h"
@@ -30,20 +36,18 @@ __device__ __forceinline__ void stamp_header(const Stamp& st) {
   st.hdr[kHdrStatus] = MOK_OK;
 }
 
-__global__ __launch_bounds__(64) void sched_count_kernel(const int32_t* __restrict__ idx, int R,
-                                                         int32_t* __restrict__ counts) {
-  const int e = blockIdx.x, lane = threadIdx.x;
-  const int n4 = R >> 2;
-  const int4* v4 = reinterpret_cast<const int4*>(idx);
-  int cnt = 0;
-  for (int i = lane; i < n4; i += 64) {
-    const int4 q = v4[i];
-    cnt += (q.x == e) + (q.y == e) + (q.z == e) + (q.w == e);
-  }
-  for (int i = (n4 << 2) + lane; i < R; i += 64) cnt += idx[i] == e;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if (lane == 0) counts[e] = cnt;
+constexpr int kSchedWaves = 16;  // waves of the scatter block
+
+__global__ __launch_bounds__(1024) void sched_hist_kernel(const int32_t* __restrict__ idx, int R, int E, int nb,
+                                                          int blk, int32_t* __restrict__ hist) {
+  __shared__ int s_h[1024];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_h[e] = 0;
+  __syncthreads();
+  const int s0 = b * blk, s1 = min(R, s0 + blk);
+  for (int s = s0 + (int)threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&s_h[idx[s]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)e * nb + b] = s_h[e];
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads); returns the
@@ -74,22 +78,32 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return ex;
 }
 
-__global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restrict__ counts, int E, int R, int BM,
-                                                          int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int R, int BM,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_start,
                                                           int32_t* __restrict__ num_tiles, int4* __restrict__ tiles,
                                                           Stamp st) {
   __shared__ int s_wave[17];
   const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
+  int c = 0;
+  if (e < E)
+    for (int b = 0; b < nb; ++b) c += hist[(int64_t)e * nb + b];
   const int nt = (c + BM - 1) / BM;
   int tot_c, tot_t;
   const int off = block_exclusive_scan(c, s_wave, &tot_c);
   const int ts = block_exclusive_scan(nt, s_wave, &tot_t);
   if (e < E) {
+    counts[e] = c;
     offsets[e] = off;
     tile_start[e] = ts;
     for (int m = 0; m < nt; ++m) tiles[ts + m] = make_int4(e, off + m * BM, min(BM, c - m * BM), 0);
+    int run = off;  // first row of e's slots from each block, blocks ascending
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i = (int64_t)e * nb + b;
+      const int h = hist[i];
+      hist[i] = run;
+      run += h;
+    }
   }
   if (e == 0) {
     offsets[E] = R;
@@ -99,47 +113,50 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restr
   }
 }
 
-__global__ __launch_bounds__(64) void sched_rank_kernel(const int32_t* __restrict__ idx, int R,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  const int e = blockIdx.x, lane = threadIdx.x;
-  const int base = offsets[e];
-  const uint64_t lt = (1ull << lane) - 1ull;
-  const int n4 = R >> 2;
-  const int4* v4 = reinterpret_cast<const int4*>(idx);
-  int running = 0;
-  for (int i0 = 0; i0 < n4; i0 += 64) {
-    const int i = i0 + lane;
-    int4 q = make_int4(-1, -1, -1, -1);
-    if (i < n4) q = v4[i];
-    const bool m0 = q.x == e, m1 = q.y == e, m2 = q.z == e, m3 = q.w == e;
-    const uint64_t b0 = __ballot(m0), b1 = __ballot(m1), b2 = __ballot(m2), b3 = __ballot(m3);
-    int r = running + __popcll(b0 & lt) + __popcll(b1 & lt) + __popcll(b2 & lt) + __popcll(b3 & lt);
-    const int s = i << 2;
-    if (m0) { perm[base + r] = s;     inv[s] = base + r;     ++r; }
-    if (m1) { perm[base + r] = s + 1; inv[s + 1] = base + r; ++r; }
-    if (m2) { perm[base + r] = s + 2; inv[s + 2] = base + r; ++r; }
-    if (m3) { perm[base + r] = s + 3; inv[s + 3] = base + r; }
-    running += __popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3);
-  }
-  for (int i0 = n4 << 2; i0 < R; i0 += 64) {
-    const int s = i0 + lane;
-    const bool m = s < R && idx[s] == e;
-    const uint64_t b = __ballot(m);
-    if (m) {
-      const int r = running + __popcll(b & lt);
-      perm[base + r] = s;
-      inv[s] = base + r;
+__global__ __launch_bounds__(1024) void sched_scatter_kernel(const int32_t* __restrict__ idx, int R, int E, int nb,
+                                                             int blk, const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int PER_WAVE = blk / kSchedWaves;  // a multiple of 64
+  __shared__ int s_w[kSchedWaves][1024];  // per-wave counts, then per-wave next row per expert
+  const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kSchedWaves * E; i += blockDim.x) s_w[i / E][i % E] = 0;
+  __syncthreads();
+  const int w0 = b * blk + wave * PER_WAVE;
+  for (int s = w0 + lane; s < min(R, w0 + PER_WAVE); s += 64) atomicAdd(&s_w[wave][idx[s]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = base[(int64_t)e * nb + b];
+    for (int w = 0; w < kSchedWaves; ++w) {
+      const int t = s_w[w][e];
+      s_w[w][e] = run;
+      run += t;
     }
-    running += __popcll(b);
+  }
+  __syncthreads();
+  for (int g = 0; g < PER_WAVE; g += 64) {
+    const int s = w0 + g + lane;
+    const int v = s < R ? idx[s] : -1;
+    int rank = 0, cnt = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int vj = __builtin_amdgcn_readlane(v, j);
+      const int eq = vj == v;
+      cnt += eq;
+      rank += eq & (j < lane);
+    }
+    if (v >= 0) {
+      const int row = s_w[wave][v] + rank;
+      perm[row] = s;
+      inv[s] = row;
+    }
+    // the last lane of each expert in this group moves that expert's next row on
+    if (v >= 0 && rank == cnt - 1) s_w[wave][v] += cnt;
   }
 }
 
-// Tiny batches (R * E <= 2^14): the three steps in one workgroup of 16 waves, with idx
-// staged in LDS; wave w counts and then ranks experts w, w + 16, ... as the per-expert
-// waves above do (ranks by ascending slot), so every output is the same; two launches
-// fewer. Measured: 64 tokens x 8 experts 11-14 -> 6 us; at 4096 routed rows x 32 experts
-// the one workgroup takes 33 us against 19 us for the three kernels, hence the bound.
+// Tiny batches (R * E <= 2^14): count, scan and rank in one workgroup of 16 waves, with
+// idx staged in LDS; wave w counts and then ranks experts w, w + 16, ... by a ballot scan
+// in ascending slot order, so every output equals the three-kernel path's; two launches
+// fewer (64 tokens x 8 experts: 11-14 -> 6 us).
 constexpr int kSchedFusedMaxR = 16384;
 
 __global__ __launch_bounds__(1024) void sched_fused_kernel(const int32_t* __restrict__ idx, int R, int E, int BM,
@@ -209,10 +226,13 @@ hipError_t launch_schedule(const Ctx& c, const int32_t* idx) {
                        c.tile_start, c.num_tiles, c.tiles, c.perm, c.inv, st);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(sched_count_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.counts);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, c.s, c.counts, c.E, c.R, c.BM, c.offsets,
+  const int blk = sched_block(c.R);
+  const int nb = (c.R + blk - 1) / blk;
+  hipLaunchKernelGGL(sched_hist_kernel, dim3(nb), dim3(1024), 0, c.s, idx, c.R, c.E, nb, blk, c.hist);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, c.s, c.hist, nb, c.E, c.R, c.BM, c.counts, c.offsets,
                      c.tile_start, c.num_tiles, c.tiles, st);
-  if (c.R > 0) hipLaunchKernelGGL(sched_rank_kernel, dim3(c.E), dim3(64), 0, c.s, idx, c.R, c.offsets, c.perm, c.inv);
+  hipLaunchKernelGGL(sched_scatter_kernel, dim3(nb), dim3(1024), 0, c.s, idx, c.R, c.E, nb, blk, c.hist, c.perm,
+                     c.inv);
   return hipGetLastError();
 }
 

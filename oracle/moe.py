@@ -23,7 +23,8 @@ import numpy as np
 
 __all__ = [
     "build_oracle", "round_to", "bf16_round", "router_logits", "router_logits_exact", "select_topk",
-    "topk_gates", "route", "schedule", "forward", "backward", "DenseWeights", "silu", "sigmoid",
+    "topk_gates", "route", "schedule", "forward", "backward", "DenseWeights", "silu", "sigmoid", "combine",
+    "reduce_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -246,12 +247,19 @@ def forward(x, weights, idx, gate, fmt: str, E: int, I: int, experts=None) -> di
         p[s] = round_to(O, fmt)
     out = dict(a=a_s, u=u_s, h=h_s, o=o, p=p)
     if experts is None:
-        g = np.asarray(gate, np.float64)
-        y = np.zeros((T, H))
-        for j in range(k):
-            y = y + g[:, j:j + 1] * p[j::k]
-        out["y"] = round_to(y, fmt)
+        out["y"] = combine(p, gate, fmt)
     return out
+
+
+def combine(p, gate, fmt: str) -> np.ndarray:
+    """Push combine: y_t = sum_{j=0..k-1} g_tj * p_{t*k+j} in slot order, stored in fmt.
+    p [T*k, H] holds every slot's stored partial row."""
+    g = np.asarray(gate, np.float64)
+    T, k = g.shape
+    y = np.zeros((T, np.asarray(p).shape[1]))
+    for j in range(k):
+        y = y + g[:, j:j + 1] * p[j::k]
+    return round_to(y, fmt)
 
 
 # ----------------------------------------------------------------------------
@@ -319,23 +327,36 @@ def backward(x, weights, wr, idx, gate, fwd, dy, fmt: str, I: int, wfmt: str = N
     out = dict(dgate=gp.reshape(T, k), dgu=dgu, q=q, dw1=dw1, dw2=dw2)
     if experts is not None:
         return out
-    gpk = gp.reshape(T, k)
+    out.update(reduce_backward(x, wr, idx, gate, gp.reshape(T, k), q, fmt, wfmt, router))
+    return out
+
+
+def reduce_backward(x, wr, idx, gate, dgate, q, fmt: str, wfmt: str, router: bool = True) -> dict:
+    """The token side of the backward once every slot's d-gate g' and stored partial row
+    q are known: dz_s = g_s (g'_s - sum_i g_ti g'_ti) (softmax over the selected logits),
+    dX_t = sum_j q_tj (+ sum_j dz_tj Wr[idx_tj]) in slot order, stored in fmt, and
+    dWr[e] = sum over e's slots of dz_s x_t, stored in wfmt (only with router)."""
+    x = np.asarray(x, np.float64)
+    g = np.asarray(gate, np.float64)
+    gpk = np.asarray(dgate, np.float64)
+    T, H = x.shape
+    k = idx.shape[1]
+    E = np.asarray(wr).shape[0]
     ssum = np.zeros(T)
     for j in range(k):
         ssum = ssum + g[:, j] * gpk[:, j]
     dz = g * (gpk - ssum[:, None])
-    out["dz"] = dz
-    wr64 = np.asarray(wr, np.float64)
+    out = dict(dz=dz)
     acc = np.zeros((T, H))
     for j in range(k):
         acc = acc + q[j::k]
     if router:
+        wr64 = np.asarray(wr, np.float64)
         for j in range(k):
             acc = acc + dz[:, j:j + 1] * wr64[idx[:, j]]
         dwr = np.zeros((E, H))
         dzf = dz.ravel()
-        for e in range(E):
-            s = by_e[e]
+        for e, s in enumerate(_slots_by_expert(idx, E)):
             if s.size:
                 dwr[e] = dzf[s] @ x[s // k]
         out["dwr"] = round_to(dwr, wfmt)

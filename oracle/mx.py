@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .moe import bf16_round, round_to, sigmoid, silu, _slots_by_expert
+from .moe import bf16_round, combine, reduce_backward, round_to, sigmoid, silu, _slots_by_expert
 
 E4M3_MAX = 448.0
 MX_BLOCK = 32
@@ -118,11 +118,7 @@ def forward_mx(x, weights, idx, gate, E: int, I: int, experts=None) -> dict:
         a_s[s], u_s[s], h_s[s], p[s] = bf16_round(A), bf16_round(U), Hh, bf16_round(O)
     if experts is not None:
         return dict(a=a_s, u=u_s, h=h_s, p=p)
-    g = np.asarray(gate, np.float64)
-    y = np.zeros((T, H))
-    for j in range(k):
-        y = y + g[:, j:j + 1] * p[j::k]
-    return dict(a=a_s, u=u_s, h=h_s, p=p, y=bf16_round(y))
+    return dict(a=a_s, u=u_s, h=h_s, p=p, y=combine(p, gate, "bf16"))
 
 
 def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, router=True, experts=None,
@@ -169,24 +165,6 @@ def backward_mx(x, weights, wr, idx, gate, fwd, dy, I: int, segments=None, route
         dw1[e] = round_to(mx_token_blocks(G, seg).T @ mx_token_blocks(x[t], seg), wfmt)
     if experts is not None:
         return dict(dgate=gp.reshape(T, k), dgu=dgu, dw1=dw1, dw2=dw2, q=q)
-    gpk = gp.reshape(T, k)
-    ssum = np.zeros(T)
-    for j in range(k):
-        ssum = ssum + g[:, j] * gpk[:, j]
-    dz = g * (gpk - ssum[:, None])
-    acc = np.zeros((T, H))
-    for j in range(k):
-        acc = acc + q[j::k]
-    out = dict(dgate=gpk, dz=dz, dgu=dgu, dw1=dw1, dw2=dw2, q=q)
-    if router:
-        wr64 = np.asarray(wr, np.float64)
-        for j in range(k):
-            acc = acc + dz[:, j:j + 1] * wr64[idx[:, j]]
-        dwr = np.zeros((E, H))
-        dzf = dz.ravel()
-        for e, s in enumerate(by_e):
-            if s.size:
-                dwr[e] = dzf[s] @ x[s // k]
-        out["dwr"] = round_to(dwr, wfmt)
-    out["dx"] = bf16_round(acc)
+    out = dict(dgate=gp.reshape(T, k), dgu=dgu, dw1=dw1, dw2=dw2, q=q)
+    out.update(reduce_backward(x, wr, idx, gate, gp.reshape(T, k), q, "bf16", wfmt, router))
     return out

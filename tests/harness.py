@@ -92,3 +92,62 @@ def run_oracle(case: Case, backward=True, BM=32, router_grad=True, wfmt=None):
         out["bwd"] = orc.backward(x, W, wr, idx, g, fwd, case.dy.float().numpy(), fmt, w.I,
                                   wfmt=wfmt or fmt, router=router_grad)
     return out
+
+
+def oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt="bf16", mx=False, workers=8):
+    """The oracle's forward and backward over all experts that have slots, evaluated as expert
+    chunks in threads (numpy releases the GIL in its large array operations) and merged;
+    then the token side: the slot-order combine and the router backward / dX reduction
+    (oracle.combine, oracle.reduce_backward). Bit for bit the oracle's whole-step result,
+    which a CPU test checks; the full-size GPU tests use it to keep the oracle's passes over
+    hundreds of experts within minutes."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=max(1, 16 // workers)):
+        return _oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt, mx, workers, ThreadPoolExecutor)
+
+
+def _oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt, mx, workers, ThreadPoolExecutor):
+    present = sorted(set(np.asarray(idx).ravel().tolist()))
+    chunks = [c for c in (present[i::workers] for i in range(workers)) if c]
+    flat = np.asarray(idx).ravel()
+
+    def rows_of(ch):
+        return np.nonzero(np.isin(flat, ch))[0]
+
+    def fwd(ch):
+        if mx:
+            return ch, orc.mx.forward_mx(x, W, idx, gate, E, I, experts=ch)
+        return ch, orc.forward(x, W, idx, gate, fmt, E, I, experts=ch)
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        fparts = list(ex.map(fwd, chunks))
+    f = {key: np.full_like(fparts[0][1][key], np.nan) for key in fparts[0][1]}
+    for ch, part in fparts:
+        r = rows_of(ch)
+        for key in f:
+            f[key][r] = part[key][r]
+    f["y"] = orc.combine(f["p"], gate, "bf16" if mx else fmt)
+
+    def bwd(ch):
+        if mx:
+            return ch, orc.mx.backward_mx(x, W, wr, idx, gate, f, dy, I, experts=ch)
+        return ch, orc.backward(x, W, wr, idx, gate, f, dy, fmt, I, experts=ch)
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        bparts = list(ex.map(bwd, chunks))
+    T, k = np.asarray(idx).shape
+    b = dict(dgate=np.full(T * k, np.nan), dgu=np.full((T * k, 2 * I), np.nan),
+             q=np.full((T * k, np.asarray(x).shape[1]), np.nan), dw1={}, dw2={})
+    for ch, part in bparts:
+        r = rows_of(ch)
+        b["dgate"][r] = part["dgate"].ravel()[r]
+        b["dgu"][r] = part["dgu"][r]
+        b["q"][r] = part["q"][r]
+        b["dw1"].update(part["dw1"])
+        b["dw2"].update(part["dw2"])
+    b["dgate"] = b["dgate"].reshape(T, k)
+    act = "bf16" if mx else fmt
+    b.update(orc.reduce_backward(x, wr, idx, gate, b["dgate"], b["q"], act, act))
+    return f, b

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle as orc
-from harness import TOL, np64, rel_fro
+from harness import TOL, np64, oracle_step_parallel, rel_fro
 from mixture_experts_layer_stable_amd import inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -30,10 +30,17 @@ N_EXP = 2          # sampled experts (whole dW1, dW2)
 
 
 class _Weights:
+    """Kept experts' weights for the oracle (fp64 on demand); prints a progress line every
+    32 weight reads, since the oracle's passes over many experts take minutes."""
+
     def __init__(self, kept):
         self.kept = kept
+        self.reads = 0
 
     def w1(self, e):
+        self.reads += 1
+        if self.reads % 32 == 0:
+            print("  oracle: %d expert weight reads" % self.reads, flush=True)
         return self.kept[e][0].float().numpy().astype(np.float64)
 
     def w2(self, e):
@@ -103,9 +110,8 @@ def _run(w):
     # ---- token subset: sampled tokens' rows, and dWr of e_wr (all of its tokens are in it)
     W = _Weights(kept)
     xs = x_cpu.float().numpy()[sub]
-    fwd = orc.forward(xs, W, idx[sub], g[sub], "bf16", w.E, w.I)
-    bwd = orc.backward(xs, W, wr_cpu.float().numpy(), idx[sub], g[sub], fwd, dy_cpu.float().numpy()[sub], "bf16",
-                       w.I)
+    fwd, bwd = oracle_step_parallel(xs, W, wr_cpu.float().numpy(), idx[sub], g[sub], dy_cpu.float().numpy()[sub],
+                                    w.E, w.I, fmt="bf16")
     pos = np.searchsorted(sub, tok)                            # sampled tokens inside the subset
     saved = buf.saved_views()
     rows = sc_g["inv"][(tok[:, None] * w.k + np.arange(w.k)[None, :]).ravel()]
@@ -120,14 +126,18 @@ def _run(w):
         "dwr[%d]" % e_wr: rel_fro(np64(buf.dwr[e_wr]), bwd["dwr"][e_wr]),
     }
 
-    # ---- sampled experts: whole dW1[e], dW2[e] over all of e's rows (all tokens)
-    xa = x_cpu.float().numpy()
-    for e in exps:
+    # ---- sampled experts: whole dW1[e], dW2[e] over all of e's rows (all tokens), one thread each
+    from concurrent.futures import ThreadPoolExecutor
+    xa, dya, wra = x_cpu.float().numpy(), dy_cpu.float().numpy(), wr_cpu.float().numpy()
+
+    def one_expert(e):
         f_e = orc.forward(xa, W, idx, g, "bf16", w.E, w.I, experts=[e])
-        b_e = orc.backward(xa, W, wr_cpu.float().numpy(), idx, g, f_e, dy_cpu.float().numpy(), "bf16", w.I,
-                           experts=[e])
-        errs["dw1[%d]" % e] = rel_fro(np64(buf.dw1[e]), b_e["dw1"][e])
-        errs["dw2[%d]" % e] = rel_fro(np64(buf.dw2[e]), b_e["dw2"][e])
+        return e, orc.backward(xa, W, wra, idx, g, f_e, dya, "bf16", w.I, experts=[e])
+
+    with ThreadPoolExecutor(len(exps)) as ex:
+        for e, b_e in ex.map(one_expert, exps):
+            errs["dw1[%d]" % e] = rel_fro(np64(buf.dw1[e]), b_e["dw1"][e])
+            errs["dw2[%d]" % e] = rel_fro(np64(buf.dw2[e]), b_e["dw2"][e])
     print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL["bf16"], (k, v)
@@ -214,17 +224,21 @@ def test_kimi_k2_mxfp8_streamed_full_size():
 
     W = _Weights(kept)
     xs, dys, wrs = x_cpu.float().numpy(), dy_cpu.float().numpy(), wr_cpu.float().numpy()
-    f = orc.mx.forward_mx(xs[sub], W, idx[sub], g[sub], w.E, w.I)
-    bw = orc.mx.backward_mx(xs[sub], W, wrs, idx[sub], g[sub], f, dys[sub], w.I)
+    f, bw = oracle_step_parallel(xs[sub], W, wrs, idx[sub], g[sub], dys[sub], w.E, w.I, mx=True)
     pos = np.searchsorted(sub, tok)
     errs = {"y": rel_fro(np64(st.y[tok]), f["y"][pos]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"][pos]),
             "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"][pos]),
             "dwr[%d]" % e_wr: rel_fro(np64(st.dwr[e_wr]), bw["dwr"][e_wr])}
-    for e in exps:
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one_expert(e):
         fe = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, experts=[e])
-        be = orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e])
-        errs["dw1[%d]" % e] = rel_fro(np64(st.dw1[e]), be["dw1"][e])
-        errs["dw2[%d]" % e] = rel_fro(np64(st.dw2[e]), be["dw2"][e])
+        return e, orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e])
+
+    with ThreadPoolExecutor(len(exps)) as ex:
+        for e, be in ex.map(one_expert, exps):
+            errs["dw1[%d]" % e] = rel_fro(np64(st.dw1[e]), be["dw1"][e])
+            errs["dw2[%d]" % e] = rel_fro(np64(st.dw2[e]), be["dw2"][e])
     print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= 2e-2, (k, v)

@@ -241,3 +241,34 @@ def test_storage_points_hand_worked_do_rounded_before_dw2():
     dy = np.array([[1.0234375], [-1.0]])
     b = orc.backward(x, W, np.zeros((1, 1)), idx, g, fwd, dy, "bf16", I, router=False)
     assert b["dw2"][0][0, 0] == 2.0 ** -6
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_expert_chunked_step_equals_whole_step(mx):
+    """The threaded, expert-chunked evaluation the full-size GPU tests use (harness.
+    oracle_step_parallel) gives the oracle's whole-step outputs bit for bit, here with an
+    expert that has no slots and chunks of unequal size."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from harness import oracle_step_parallel
+    T, H, E, k, I = 40, 32, 7, 3, 32
+    x, wr, w1, w2, bias, dy = _problem(T=T, H=H, E=E, k=k, I=I, seed=5)
+    bias[6] = -50.0                                  # expert 6 gets no slots
+    x, dy = orc.bf16_round(x), orc.bf16_round(dy)
+    z, idx, g = _route_exact(x, wr, bias, k)
+    W = orc.DenseWeights(orc.bf16_round(w1), orc.bf16_round(w2))
+    if mx:
+        f0 = orc.mx.forward_mx(x, W, idx, g, E, I)
+        b0 = orc.mx.backward_mx(x, W, wr, idx, g, f0, dy, I)
+    else:
+        f0 = orc.forward(x, W, idx, g, "bf16", E, I)
+        b0 = orc.backward(x, W, wr, idx, g, f0, dy, "bf16", I)
+    f1, b1 = oracle_step_parallel(x, W, wr, idx, g, dy, E, I, mx=mx, workers=3)
+    for key in ("a", "u", "h", "p", "y"):
+        np.testing.assert_array_equal(f1[key], f0[key], err_msg=key)
+    for key in ("dgate", "dgu", "q", "dx", "dwr", "dz"):
+        np.testing.assert_array_equal(b1[key], b0[key], err_msg=key)
+    for e in range(E):
+        if e in b1["dw1"]:
+            np.testing.assert_array_equal(b1["dw1"][e], b0["dw1"][e])
+            np.testing.assert_array_equal(b1["dw2"][e], b0["dw2"][e])
