@@ -219,18 +219,20 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   constexpr bool IN_RING = Tl::NW * PATCH <= SB;
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
   __shared__ __align__(1024) char smem[STAGES * SB + (IN_RING ? 0 : Tl::NW * PATCH)];
+  __shared__ int s_u[kMaxE2 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   char* patch = smem + (IN_RING ? (STAGES - 1) * SB : STAGES * SB) + wave * PATCH;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
-  const int64_t total = (int64_t)E * MT * NT;
   const int P = min(8, (int)gridDim.x);
   const int xcd = blockIdx.x % P;
   const int nx = ((int)gridDim.x - xcd + P - 1) / P;
   const int li = blockIdx.x / P;
-  const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
+  if (guard_fail(a.guard)) return;
+  int64_t lo, hi;
+  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.counts[e] + 31) / 32; }, s_u, P, xcd, lo, hi);
   int64_t L = lo + li;
-  if (L >= hi || guard_fail(a.guard)) return;
+  if (L >= hi) return;
   OA oa;
   OB ob;
   int e = 0, mt = 0, nt = 0, KT = 0;
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
       ring_prologue<STAGES>(oa, ob, KT, smem, wave);
     }
     epilogue_bf16<Tl>(acc, patch, wm, wn, lane,
-                      [&](int row, int col, const uint4& v) { stg16(out + (int64_t)row * a.N + col, v); });
+                      [&](int row, int col, const uint4& v) { stg16_nt(out + (int64_t)row * a.N + col, v); });
     if (Ln >= hi) break;
     L = Ln;
     first = false;

@@ -380,18 +380,21 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
   static_assert(Tl::NW * kBf16PatchBytes <= STG, "epilogue patches fit in one ring stage");
   __shared__ __align__(1024) char smem[STAGES * STG];
+  __shared__ int s_u[kMaxEx + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   char* patch = smem + (STAGES - 1) * STG + wave * kBf16PatchBytes;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
-  const int64_t total = (int64_t)E * MT * NT;
   const int P = min(8, (int)gridDim.x);
   const int xcd = blockIdx.x % P;
   const int nx = ((int)gridDim.x - xcd + P - 1) / P;
   const int li = blockIdx.x / P;
-  const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
+  if (guard_fail(a.guard)) return;
+  int64_t lo, hi;
+  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.pofs[e + 1] - a.pofs[e]) / 128; }, s_u, P, xcd, lo,
+                   hi);
   int64_t L = lo + li;
-  if (L >= hi || guard_fail(a.guard)) return;
+  if (L >= hi) return;
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
   const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
   OA oa;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
       mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
     }
     epilogue_bf16<Tl>(acc, patch, wm, wn, lane,
-                      [&](int row, int col, const uint4& v) { stg16(out + (int64_t)row * a.N + col, v); });
+                      [&](int row, int col, const uint4& v) { stg16_nt(out + (int64_t)row * a.N + col, v); });
     if (Ln >= hi) break;
     L = Ln;
     first = false;
