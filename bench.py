@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-m", type=int, default=0, help="schedule tile rows (0 = two-wave rule)")
+    ap.add_argument("--replay", action="store_true",
+                    help="forward-activation replay: keep no activations, form them again in the backward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (known bytes, for HBM counter scaling)")
     args = ap.parse_args()
@@ -237,7 +239,7 @@ def main():
     if mx:
         M = w.micro_batches
         d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=args.tile_m, mb_count=M,
-                     ring=2)
+                     ring=2, flags=mok.FLAG_REPLAY if args.replay else 0)
         q = mok.MxWeights(d, "cuda")
         mok.weights_quantize(d, w1, w2, q)
         torch.cuda.synchronize()
@@ -249,7 +251,8 @@ def main():
         def step():
             st.run(x, wr, bias, q, dy)
     else:
-        d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=args.tile_m)
+        d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=args.tile_m,
+                     flags=mok.FLAG_REPLAY if args.replay else 0)
         buf = mok.Buffers(d, "cuda", backward=True)
 
         def step():
@@ -317,6 +320,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "routing": "zipf-imbalanced" if w.zipf else "near-uniform", "tile_m": d.c().tile_m or "auto",
+                   **({"activations": "replayed"} if args.replay else {}),
                    **({"micro_batches": w.micro_batches, "ring_slots": 2} if mx else {})},
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},

@@ -91,6 +91,13 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
 #define MOK_FLAG_WGRAD_DEFER 2u /* MXFP8 backward: stash this micro-batch's weight-gradient
                                    operands only; dw1, dw2, dwr are not touched (see
                                    mok_moe_backward) */
+#define MOK_FLAG_REPLAY 4u      /* forward-activation replay: the forward keeps nothing for the
+                                   backward (mok_sizes.saved = 0, `saved` may be NULL; a, u, h
+                                   are formed in the forward workspace) and the backward forms
+                                   a, u, h again with the forward's own kernels from x (one
+                                   more FC1 GEMM, MXFP8: also the x quantiser) before the
+                                   dH GEMM; every output is bit-identical to the stored path.
+                                   Forward and backward of one step must agree on the flag. */
 
 /*
  * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;

@@ -18,6 +18,7 @@ int elem_size(int act) { return act == MOK_F32 ? 4 : 2; }
 int mb_count_of(const mok_desc* d) { return d->mb_count > 0 ? d->mb_count : 1; }
 int ring_of(const mok_desc* d) { return d->ring > 0 ? d->ring : 1; }
 bool is_mx(const mok_desc* d) { return d->gemm == MOK_MXFP8; }
+bool is_replay(const mok_desc* d) { return (d->flags & MOK_FLAG_REPLAY) != 0; }
 
 // Rows of the token-axis operands of the MXFP8 weight-gradient GEMMs: every
 // expert's rows of the step padded to a multiple of 128.
@@ -84,6 +85,7 @@ struct Layout {
   size_t counts, offsets, tile_start, num_tiles, perm, inv, tiles, hist, sched;  // header at 0
   size_t au, h, saved;
   size_t fwd_part, fwd;
+  size_t fau, fh, bau, bh;  // replay: a|u and h in the forward and the backward workspaces
   size_t dgu, bpart, dgp, dz, xs, dos, bwd;
 };
 
@@ -109,9 +111,13 @@ Layout layout_of(const mok_desc* d, int BM) {
   o = 0;
   L.au = o; o = up(o + es * (size_t)R * 2 * d->I);
   L.h = o; o = up(o + es * (size_t)R * d->I);
-  L.saved = o;
+  const size_t act_bytes = o;  // a|u then h
+  L.saved = is_replay(d) ? 0 : act_bytes;
   L.fwd_part = 0;
   L.fwd = up(es * (size_t)R * d->H);
+  L.fau = L.fwd + L.au;
+  L.fh = L.fwd + L.h;
+  if (is_replay(d)) L.fwd += act_bytes;
   o = 0;
   L.dgu = o; o = up(o + es * (size_t)R * 2 * d->I);
   L.bpart = o; o = up(o + es * (size_t)R * d->H);
@@ -121,6 +127,9 @@ Layout layout_of(const mok_desc* d, int BM) {
   const size_t rows = d->act == MOK_BF16 ? es * (size_t)R * d->H : 0;
   L.xs = o; o = up(o + rows);
   L.dos = o; o = up(o + rows);
+  L.bau = o + L.au;
+  L.bh = o + L.h;
+  if (is_replay(d)) o += act_bytes;
   L.bwd = o;
   return L;
 }
@@ -130,8 +139,8 @@ Layout layout_of(const mok_desc* d, int BM) {
 // Then the stash of all micro-batches (array-major: micro-batch m's part of each
 // array at its m-th R rows) and the flush buffers.
 struct MxLayout {
-  size_t xq, xs, hq, hs, part, fslot, fwd;
-  size_t dyq, dys, dguq, dgus, bpart, dgp, bslot;
+  size_t xq, xs, hq, hs, part, rau, rh, fslot, fwd;
+  size_t dyq, dys, dguq, dgus, bpart, dgp, bxq, bxs, bhq, bhs, bau, bh, bslot;
   size_t st_counts, st_offsets, st_perm, st_dz, st_xs, st_dos, st_h, st_dgu;
   size_t gcnt, pofs, rowmap, xt, xts, dot, dots, ht, hts, dgut, dguts, dwrp, bwd;
   int64_t kmax;
@@ -147,6 +156,10 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.hq = o; o = up(o + (size_t)(R * I));
   L.hs = o; o = up(o + (size_t)(R * I / 32));
   L.part = o; o = up(o + (size_t)(2 * R * H));
+  // replay: a|u and h of this micro-batch live in the slot instead of `saved`
+  const size_t rp = is_replay(d) ? 1 : 0;
+  L.rau = o; o = up(o + rp * (size_t)(2 * R * 2 * I));
+  L.rh = o; o = up(o + rp * (size_t)(2 * R * I));
   L.fslot = o;
   L.fwd = (size_t)S * L.fslot;
   o = 0;
@@ -156,6 +169,13 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.dgus = o; o = up(o + (size_t)(R * 2 * I / 32));
   L.bpart = o; o = up(o + (size_t)(2 * R * H));
   L.dgp = o; o = up(o + (size_t)(4 * R * dgate_parts(d->I)));
+  // replay: the backward forms quantised x, a|u, h (and quantised h) again in its slot
+  L.bxq = o; o = up(o + rp * (size_t)(T * H));
+  L.bxs = o; o = up(o + rp * (size_t)(T * H / 32));
+  L.bhq = o; o = up(o + rp * (size_t)(R * I));
+  L.bhs = o; o = up(o + rp * (size_t)(R * I / 32));
+  L.bau = o; o = up(o + rp * (size_t)(2 * R * 2 * I));
+  L.bh = o; o = up(o + rp * (size_t)(2 * R * I));
   L.bslot = o;
   o = (size_t)S * L.bslot;
   L.st_counts = o; o = up(o + (size_t)(4 * M * E));
@@ -309,11 +329,12 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
   if (wr != nullptr && !aligned16(wr)) return MOK_ERR_ALIGN;
   MOK_REQUIRE(ws);
   const mok_mx_weights* q = w->mx;
+  const bool replay = is_replay(d);
   if (c.R > 0) {
     MOK_REQUIRE(x);
     MOK_REQUIRE(idx);
     MOK_REQUIRE(gate);
-    MOK_REQUIRE(saved);
+    if (!replay) MOK_REQUIRE(saved);
     MOK_REQUIRE(dy);
     MOK_REQUIRE(dx);
     MOK_REQUIRE(dgate);
@@ -322,19 +343,29 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
     MOK_REQUIRE(q->w2ts);
     MOK_REQUIRE(q->w1tq);
     MOK_REQUIRE(q->w1ts);
+    if (replay) {
+      MOK_REQUIRE(q->w1q);
+      MOK_REQUIRE(q->w1s);
+    }
   }
   const Layout L = layout_of(d, c.BM);
   const MxLayout X = mx_layout_of(d);
-  const char* sv = (const char*)saved;
   char* wb = (char*)ws;
   char* bs = wb + (size_t)(d->mb_index % ring_of(d)) * X.bslot;
+  const char* au = replay ? bs + X.bau : (const char*)saved + L.au;
+  const char* hr = replay ? bs + X.bh : (const char*)saved + L.h;
   const int64_t m = d->mb_index, R = c.R, H = c.H, I = c.I, E = c.E;
   float* dz = (float*)(wb + X.st_dz) + m * R;
   char* st_dgu = wb + X.st_dgu + (size_t)(m * R * 2 * I * 2);
   if (c.R > 0) {
     float* dgp = (float*)(bs + X.dgp);
+    if (replay) {  // the forward's x quantiser and FC1, again
+      MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, x, c.T, c.H, bs + X.bxq, bs + X.bxs, c.T));
+      MOK_LAUNCH("fc1", c.s, launch_fc1_mx(c, bs + X.bxq, bs + X.bxs, q->w1q, q->w1s, bs + X.bau, bs + X.bh,
+                                           bs + X.bhq, bs + X.bhs));
+    }
     MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, dy, c.T, c.H, bs + X.dyq, bs + X.dys, c.T));
-    MOK_LAUNCH("dh", c.s, launch_dh_mx(c, bs + X.dyq, bs + X.dys, q->w2tq, q->w2ts, sv + L.au, sv + L.h, gate, st_dgu,
+    MOK_LAUNCH("dh", c.s, launch_dh_mx(c, bs + X.dyq, bs + X.dys, q->w2tq, q->w2ts, au, hr, gate, st_dgu,
                                        bs + X.dguq, bs + X.dgus, dgp));
     MOK_LAUNCH("router_bwd", c.s, launch_router_bwd(c, dgp, gate, dgate, dz));
     MOK_LAUNCH("dx", c.s, launch_dx_mx(c, bs + X.dguq, bs + X.dgus, q->w1tq, q->w1ts, bs + X.bpart));
@@ -342,7 +373,7 @@ mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int
     // stash: routed-order x and dO = g*dy rows, h rows, perm
     MOK_LAUNCH("quant", c.s, launch_gather_rows(c, x, nullptr, wb + X.st_xs + (size_t)(m * R * H * 2)));
     MOK_LAUNCH("quant", c.s, launch_gather_rows(c, dy, gate, wb + X.st_dos + (size_t)(m * R * H * 2)));
-    MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_h + (size_t)(m * R * I * 2), sv + L.h, (size_t)(R * I * 2),
+    MOK_LAUNCH("quant", c.s, hipMemcpyAsync(wb + X.st_h + (size_t)(m * R * I * 2), hr, (size_t)(R * I * 2),
                                             hipMemcpyDeviceToDevice, c.s));
   }
   MOK_LAUNCH("quant", c.s, launch_stash_sched(c, (int32_t*)(wb + X.st_counts) + m * E,
@@ -493,10 +524,11 @@ mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const 
   MOK_REQUIRE(x);
   MOK_REQUIRE(gate);
   MOK_REQUIRE(y);
-  MOK_REQUIRE(saved);
+  if (!is_replay(d)) MOK_REQUIRE(saved);
   MOK_REQUIRE(ws);
   const Layout L = layout_of(d, c.BM);
-  char* sv = (char*)saved;
+  char* au = is_replay(d) ? (char*)ws + L.fau : (char*)saved + L.au;
+  char* hr = is_replay(d) ? (char*)ws + L.fh : (char*)saved + L.h;
   if (is_mx(d)) {
     const mok_mx_weights* q = w->mx;
     if (q == nullptr) return MOK_ERR_NULL;
@@ -506,17 +538,20 @@ mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const 
     MOK_REQUIRE(q->w2s);
     const MxLayout X = mx_layout_of(d);
     char* fs = (char*)ws + (size_t)(d->mb_index % ring_of(d)) * X.fslot;
+    if (is_replay(d)) {
+      au = fs + X.rau;
+      hr = fs + X.rh;
+    }
     MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, x, c.T, c.H, fs + X.xq, fs + X.xs, c.T));
-    MOK_LAUNCH("fc1", c.s, launch_fc1_mx(c, fs + X.xq, fs + X.xs, q->w1q, q->w1s, sv + L.au, sv + L.h, fs + X.hq,
-                                         fs + X.hs));
+    MOK_LAUNCH("fc1", c.s, launch_fc1_mx(c, fs + X.xq, fs + X.xs, q->w1q, q->w1s, au, hr, fs + X.hq, fs + X.hs));
     MOK_LAUNCH("fc2", c.s, launch_fc2_mx(c, fs + X.hq, fs + X.hs, q->w2q, q->w2s, fs + X.part));
     MOK_LAUNCH("combine", c.s, launch_combine(c, fs + X.part, gate, y));
     return MOK_OK;
   }
   MOK_REQUIRE(w->w1);
   MOK_REQUIRE(w->w2);
-  MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, sv + L.au, sv + L.h));
-  MOK_LAUNCH("fc2", c.s, launch_fc2(c, sv + L.h, w->w2, ws));
+  MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, au, hr));
+  MOK_LAUNCH("fc2", c.s, launch_fc2(c, hr, w->w2, ws));
   MOK_LAUNCH("combine", c.s, launch_combine(c, ws, gate, y));
   return MOK_OK;
 }
@@ -556,19 +591,22 @@ mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const
     MOK_REQUIRE(gate);
     MOK_REQUIRE(w->w1);
     MOK_REQUIRE(w->w2);
-    MOK_REQUIRE(saved);
+    if (!is_replay(d)) MOK_REQUIRE(saved);
     MOK_REQUIRE(dy);
     MOK_REQUIRE(dx);
     MOK_REQUIRE(dgate);
     MOK_REQUIRE(ws);
   }
   const Layout L = layout_of(d, c.BM);
-  const char* sv = (const char*)saved;
   char* wb = (char*)ws;
+  const bool replay = is_replay(d);
+  char* au = replay ? wb + L.bau : (char*)saved + L.au;
+  char* hr = replay ? wb + L.bh : (char*)saved + L.h;
   float* dgp = (float*)(wb + L.dgp);
   float* dz = (float*)(wb + L.dz);
   if (c.R > 0) {
-    MOK_LAUNCH("dh", c.s, launch_dh(c, dy, w->w2, sv + L.au, sv + L.h, gate, wb + L.dgu, dgp));
+    if (replay) MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, au, hr));  // the forward's FC1, again
+    MOK_LAUNCH("dh", c.s, launch_dh(c, dy, w->w2, au, hr, gate, wb + L.dgu, dgp));
     MOK_LAUNCH("router_bwd", c.s, launch_router_bwd(c, dgp, gate, dgate, dz));
     MOK_LAUNCH("dx", c.s, launch_dx(c, wb + L.dgu, w->w1, wb + L.bpart));
     MOK_LAUNCH("dx_reduce", c.s, launch_dx_reduce(c, wb + L.bpart, dz, idx, wr, dx));
@@ -576,10 +614,10 @@ mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const
   if (c.act == MOK_BF16) {
     MOK_LAUNCH("gather", c.s, launch_gather_rows(c, dy, gate, wb + L.dos));
     MOK_LAUNCH("gather", c.s, launch_gather_rows(c, x, nullptr, wb + L.xs));
-    MOK_LAUNCH("dw2", c.s, launch_dw2_bf16(c, wb + L.dos, sv + L.h, dw2));
+    MOK_LAUNCH("dw2", c.s, launch_dw2_bf16(c, wb + L.dos, hr, dw2));
     MOK_LAUNCH("dw1", c.s, launch_dw1_bf16(c, wb + L.dgu, wb + L.xs, dw1));
   } else {
-    MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, sv + L.h, dw2));
+    MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, hr, dw2));
     MOK_LAUNCH("dw1", c.s, launch_dw1(c, wb + L.dgu, x, dw1));
   }
   if (dwr != nullptr) MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr));

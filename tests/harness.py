@@ -37,12 +37,13 @@ class Case:
         self.dy = inputs.make_dy(w) if dy is None else dy
 
 
-def run_gpu(case: Case, backward=True, tile_m=0, grid=0, router_grad=True, wgrad_f32=False, logits=True):
+def run_gpu(case: Case, backward=True, tile_m=0, grid=0, router_grad=True, wgrad_f32=False, logits=True,
+            replay=False):
     from mixture_experts_layer_stable_amd import mok
     w = case.w
     dev = "cuda"
     d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=tile_m, grid=grid,
-                 flags=mok.FLAG_WGRAD_F32 if wgrad_f32 else 0)
+                 flags=(mok.FLAG_WGRAD_F32 if wgrad_f32 else 0) | (mok.FLAG_REPLAY if replay else 0))
     buf = mok.Buffers(d, dev, backward=backward, wgrad_f32=wgrad_f32)
     x = case.x.to(dev)
     wr = case.wr.to(dev)
@@ -68,8 +69,9 @@ def run_gpu(case: Case, backward=True, tile_m=0, grid=0, router_grad=True, wgrad
                tiles=sv["tiles"].cpu().numpy(), tile_m=sv["tile_m"])
     if logits:
         out["logits"] = lg.cpu().numpy()
-    saved = buf.saved_views()
-    out.update(a=saved["a"].cpu(), u=saved["u"].cpu(), h=saved["h"].cpu())
+    if not replay:
+        saved = buf.saved_views()
+        out.update(a=saved["a"].cpu(), u=saved["u"].cpu(), h=saved["h"].cpu())
     if backward:
         out.update(dx=buf.dx.cpu(), dw1=buf.dw1.cpu(), dw2=buf.dw2.cpu(), dgate=buf.dgate.cpu().numpy())
         if router_grad:

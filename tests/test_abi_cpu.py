@@ -186,3 +186,18 @@ def test_noalloc_forward_refuses_oversized_workspace_before_launch(mok):
     st = mok._lib.mok_moe_forward_noalloc(ctypes.byref(d.c()), P(4096), P(4096), P(4096), ctypes.byref(w), P(4096),
                                           P(4096), 1 << 40, None)
     assert st == mok.ERR_WORKSPACE
+
+
+def test_replay_keeps_nothing_for_the_backward(mok):
+    """MOK_FLAG_REPLAY: mok_sizes.saved is 0; the forward workspace holds a, u, h instead
+    and the backward workspace has room to form them again (bf16, fp32 and MXFP8)."""
+    for kw in (dict(), dict(act=mok.F32), dict(gemm=mok.MXFP8, mb_count=4, ring=2)):
+        d = _d(mok, T=256, H=256, E=8, k=2, I=128, **kw)
+        base = mok.workspace_query(d)
+        d.flags |= mok.FLAG_REPLAY
+        rp = mok.workspace_query(d)
+        es = 4 if d.act == mok.F32 else 2
+        act = es * d.R * 3 * d.I
+        assert base["saved"] >= act and rp["saved"] == 0
+        assert rp["fwd_ws"] >= base["fwd_ws"] + act
+        assert rp["bwd_ws"] >= base["bwd_ws"] + act

@@ -105,10 +105,10 @@ def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True, wgrad_f32=Fa
     return out
 
 
-def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0):
+def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0, flags=0):
     mok = _mok()
     d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m, mb_count=M, ring=ring,
-                 grid=grid)
+                 grid=grid, flags=flags)
     st = mok.StreamedStep(d, DEV)
     q = mok.MxWeights(d, DEV)
     mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
@@ -400,3 +400,18 @@ def test_mx_step_quantisers_bit_exact():
             tot += fr
         fracs[name] = tot
     print("blocks compared:", {k_: "%.3f" % v for k_, v in fracs.items()}, flush=True)
+
+
+def test_mx_replay_streamed_bit_identical():
+    """Forward-activation replay with the streamed MXFP8 step (4 micro-batches, 2-slot ring):
+    the backward of each micro-batch quantises x and runs FC1 again; every output equals the
+    stored path's bit for bit."""
+    mok = _mok()
+    w = inputs.replace(MX_CASES["imbalanced"], T=1024)
+    x, dy, wr, b, w1, w2 = _case(w)
+    ref = _run_streamed(w, 4, 2, x, dy, wr, b, w1, w2)
+    got = _run_streamed(w, 4, 2, x, dy, wr, b, w1, w2, flags=mok.FLAG_REPLAY)
+    for n in ref:
+        a, c = got[n], ref[n]
+        same = np.array_equal(a, c) if isinstance(a, np.ndarray) else torch.equal(a, c)
+        assert same, n

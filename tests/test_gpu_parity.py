@@ -247,3 +247,22 @@ def test_schedule_built_for_another_descriptor_is_rejected():
         mok.schedule_build(d_b, buf.idx, buf.sched)
         torch.cuda.synchronize()
         assert mok.schedule_status(d_b, buf.sched) == 0
+
+
+@pytest.mark.parametrize("name,kw", [("small_bf16", {}), ("imbalanced_bf16", dict(T=600, E=12, k=3)),
+                                     ("tiny_fp32", dict(backward=True))])
+def test_replay_bit_identical(name, kw):
+    """Forward-activation replay (MOK_FLAG_REPLAY): the forward keeps no activations and the
+    backward forms a, u, h again with the forward's FC1; every output equals the stored
+    path's bit for bit."""
+    from mixture_experts_layer_stable_amd import mok
+    w = _w(name, **kw)
+    case = Case(w)
+    ref = run_gpu(case, backward=True)
+    got = run_gpu(case, backward=True, replay=True)
+    for key in ("idx", "gate", "perm", "dgate"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    for key in ("y", "dx", "dw1", "dw2", "dwr"):
+        a, b = got[key], ref[key]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), key
