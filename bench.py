@@ -31,6 +31,7 @@ METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; grouped-GEMM MFMA util %"
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 GEMMS = ("fc1", "fc2", "dh", "dx", "dw2", "dw1")
+FUSED = ("forward_fused", "backward_fused")  # whole passes in one persistent launch (their GEMMs and the rest)
 # Compulsory-work bound of one whole step (ms): the larger of the expert-GEMM flops at the
 # dense MFMA peak and the compulsory HBM bytes (weights once per pass, or once per
 # micro-batch when streamed; activations once) at 8 TB/s. 2048-token bf16 steps: 0.46 GB
@@ -45,7 +46,8 @@ def launch_flops(w, name):
     """Flops of one launch of an expert GEMM (row GEMMs: one micro-batch; dW: the step)."""
     M = max(1, w.micro_batches)
     R = (w.T // M) * w.k
-    per_row = {"fc1": 4, "fc2": 2, "dh": 2, "dx": 4, "dw2": 2 * M, "dw1": 4 * M}[name]
+    per_row = {"fc1": 4, "fc2": 2, "dh": 2, "dx": 4, "dw2": 2 * M, "dw1": 4 * M,
+               "forward_fused": 6, "backward_fused": 12}[name]
     return per_row * R * w.H * w.I
 
 
@@ -65,7 +67,7 @@ def kernel_work(w, name, active_experts=None):
     T, H, I, E = w.T // M, w.H, w.I, w.E
     R = T * w.k
     es = 4 if w.act == "f32" else 2
-    flops = {k: launch_flops(w, k) for k in GEMMS}
+    flops = {k: launch_flops(w, k) for k in GEMMS + FUSED}
     if w.gemm == "mxfp8" and name in ("fc1", "fc2", "dh", "dx"):
         q = 33.0 / 32.0  # E4M3 byte + one scale byte per 32
         ae = E if active_experts is None else active_experts
@@ -204,6 +206,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-m", type=int, default=0, help="schedule tile rows (0 = two-wave rule)")
+    ap.add_argument("--fused", action="store_true",
+                    help="one persistent launch per pass (bf16, 32-row schedule tiles)")
     ap.add_argument("--replay", action="store_true",
                     help="forward-activation replay: keep no activations, form them again in the backward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -252,7 +256,7 @@ def main():
             st.run(x, wr, bias, q, dy)
     else:
         d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=args.tile_m,
-                     flags=mok.FLAG_REPLAY if args.replay else 0)
+                     flags=(mok.FLAG_REPLAY if args.replay else 0) | (mok.FLAG_FUSED if args.fused else 0))
         buf = mok.Buffers(d, "cuda", backward=True)
 
         def step():
@@ -301,7 +305,7 @@ def main():
         achieved = work / (dom_ms * 1e-3) / 1e9
         unit = "GB/s"
     traffic = measured_traffic(dominant, w.name)
-    gemm_ms = sum(per.get(k, 0.0) for k in GEMMS)
+    gemm_ms = sum(per.get(k, 0.0) for k in GEMMS + FUSED)
     gemm_flops = sum(launches_per_step(w, k) * launch_flops(w, k) for k in GEMMS)
     mfma_util = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (MFMA_PEAK_TFLOPS[gdt] * 1e12) if gemm_ms else None
 
@@ -321,6 +325,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "routing": "zipf-imbalanced" if w.zipf else "near-uniform", "tile_m": d.c().tile_m or "auto",
                    **({"activations": "replayed"} if args.replay else {}),
+                   **({"launches": "one persistent kernel per pass"} if args.fused else {}),
                    **({"micro_batches": w.micro_batches, "ring_slots": 2} if mx else {})},
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},

@@ -98,6 +98,22 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
                                    more FC1 GEMM, MXFP8: also the x quantiser) before the
                                    dH GEMM; every output is bit-identical to the stored path.
                                    Forward and backward of one step must agree on the flag. */
+#define MOK_FLAG_FUSED 8u       /* one persistent launch per pass (the pages' single megakernel,
+                                   aikraft.ru MoK article, section 01): mok_moe_forward runs
+                                   FC1 -> FC2 -> combine, mok_moe_backward runs dH and the row
+                                   gathers -> router backward -> dX, the weight gradients and
+                                   dWr -> the dX reduction, as stages of one kernel with one
+                                   workgroup per compute unit, separated by grid barriers
+                                   whose words live in the schedule buffer. Same arithmetic
+                                   and bits as the separate kernels. Requires act = gemm =
+                                   MOK_BF16, a 32-row schedule tile (the two-wave rule picks
+                                   it below about 16k routed rows, or tile_m = 32),
+                                   k * I / 32 <= 2048 and no MOK_FLAG_WGRAD_F32: else
+                                   MOK_ERR_SHAPE or MOK_ERR_DTYPE. The workgroups must be
+                                   resident together: no other kernel may hold compute units
+                                   during the launch. A barrier that does not complete within
+                                   its bounded wait leaves MOK_ERR_HIP in the schedule
+                                   header's status word; rebuild the schedule after that. */
 
 /*
  * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;
@@ -171,6 +187,8 @@ typedef struct mok_sizes {
 } mok_sizes;
 
 /* Byte offsets of the schedule table's parts inside the schedule buffer.
+ * (After the header come the grid-barrier words of MOK_FLAG_FUSED, and after the
+ * tiles the build's scratch; neither is listed here.)
  *   header int32[16] at offset 0: [0] 0x4D4F4B53, [1] descriptor hash, [2] tile
  *                              height, [3] tile capacity, [4] status (MOK_OK after
  *                              mok_schedule_build; MOK_ERR_SCHEDULE_MISMATCH once a

@@ -19,6 +19,15 @@ int mb_count_of(const mok_desc* d) { return d->mb_count > 0 ? d->mb_count : 1; }
 int ring_of(const mok_desc* d) { return d->ring > 0 ? d->ring : 1; }
 bool is_mx(const mok_desc* d) { return d->gemm == MOK_MXFP8; }
 bool is_replay(const mok_desc* d) { return (d->flags & MOK_FLAG_REPLAY) != 0; }
+bool is_fused(const mok_desc* d) { return (d->flags & MOK_FLAG_FUSED) != 0; }
+
+// The fused persistent kernels run the bf16 path on 32-row tiles only.
+mok_status check_fused(const mok_desc* d, const Ctx& c) {
+  if (!is_fused(d)) return MOK_OK;
+  if (d->act != MOK_BF16 || d->gemm != MOK_BF16 || (d->flags & MOK_FLAG_WGRAD_F32)) return MOK_ERR_DTYPE;
+  if (c.BM != 32 || (int64_t)d->k * dgate_parts(d->I) > kFusedMaxSlotParts) return MOK_ERR_SHAPE;
+  return MOK_OK;
+}
 
 // Rows of the token-axis operands of the MXFP8 weight-gradient GEMMs: every
 // expert's rows of the step padded to a multiple of 128.
@@ -98,7 +107,7 @@ Layout layout_of(const mok_desc* d, int BM) {
   L.BM = BM;
   L.max_tiles = (int)(R / BM + std::min<int64_t>(d->E, R));
   const int64_t worst_tiles = R / 32 + std::min<int64_t>(d->E, R);
-  size_t o = up(64);  // header int32[16]
+  size_t o = up(kSchedHeaderBytes);  // header int32[16], then the fused kernels' barrier lines
   L.counts = o; o = up(o + 4 * (size_t)d->E);
   L.offsets = o; o = up(o + 4 * (size_t)(d->E + 1));
   L.tile_start = o; o = up(o + 4 * (size_t)(d->E + 1));
@@ -550,6 +559,11 @@ mok_status mok_moe_forward(const mok_desc* d, void* sched, const void* x, const 
   }
   MOK_REQUIRE(w->w1);
   MOK_REQUIRE(w->w2);
+  if ((st = check_fused(d, c)) != MOK_OK) return st;
+  if (is_fused(d)) {
+    MOK_LAUNCH("forward_fused", c.s, launch_forward_fused(c, x, w->w1, w->w2, au, hr, ws, gate, y));
+    return MOK_OK;
+  }
   MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, au, hr));
   MOK_LAUNCH("fc2", c.s, launch_fc2(c, hr, w->w2, ws));
   MOK_LAUNCH("combine", c.s, launch_combine(c, ws, gate, y));
@@ -604,6 +618,14 @@ mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const
   char* hr = replay ? wb + L.bh : (char*)saved + L.h;
   float* dgp = (float*)(wb + L.dgp);
   float* dz = (float*)(wb + L.dz);
+  if ((st = check_fused(d, c)) != MOK_OK) return st;
+  if (is_fused(d) && c.R > 0) {
+    if (replay) MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, au, hr));
+    MOK_LAUNCH("backward_fused", c.s, launch_backward_fused(c, x, idx, gate, w->w1, w->w2, wr, au, hr, dy,
+                                                            wb + L.dgu, wb + L.bpart, dgp, dz, wb + L.xs,
+                                                            wb + L.dos, dx, dw1, dw2, dgate, dwr));
+    return MOK_OK;
+  }
   if (c.R > 0) {
     if (replay) MOK_LAUNCH("fc1", c.s, launch_fc1(c, x, w->w1, au, hr));  // the forward's FC1, again
     MOK_LAUNCH("dh", c.s, launch_dh(c, dy, w->w2, au, hr, gate, wb + L.dgu, dgp));

@@ -98,6 +98,29 @@ __device__ __forceinline__ void stg16(void* p, const uint4& v) { *reinterpret_ca
 // hdr == nullptr: no schedule involved (weight quantisation), never fails.
 constexpr int kHdrHash = 1, kHdrStatus = 4;
 
+// Grid-barrier words of the fused kernels, after the 64-byte header in 128-byte lines
+// (32 int32 each; line 0 is the header's), so that the atomics of different XCCs do not
+// queue on one line: line 1 counts the XCCs that have left (word 1) and the XCC
+// arrivals at the barriers (word 2); line 2 + x counts the arrivals (word 0), the
+// workgroups (1) and the exits (2) of XCC x; line 18 + x holds the release generation
+// of XCC x; line 34 + q is work queue q (the next item to hand out). mok_schedule_build
+// zeroes them; the last workgroup to leave a fused kernel zeroes them again.
+constexpr int kSyncLine = 32, kSyncXcc = 16, kSyncQueues = 4;
+constexpr int kSyncArrive = 2, kSyncRelease = 2 + kSyncXcc, kSyncQueue = 2 + 2 * kSyncXcc;
+constexpr int kSyncLines = kSyncQueue + kSyncQueues;
+constexpr size_t kSchedHeaderBytes = (size_t)kSyncLines * kSyncLine * 4;
+
+__device__ __forceinline__ void sync_zero(int32_t* hdr) {
+  int32_t* l1 = hdr + kSyncLine;
+  l1[0] = l1[1] = l1[2] = 0;
+  for (int x = 0; x < kSyncXcc; ++x) {
+    int32_t* la = hdr + (kSyncArrive + x) * kSyncLine;
+    la[0] = la[1] = la[2] = 0;
+    hdr[(kSyncRelease + x) * kSyncLine] = 0;
+  }
+  for (int q = 0; q < kSyncQueues; ++q) hdr[(kSyncQueue + q) * kSyncLine] = 0;
+}
+
 struct Guard {
   int32_t* hdr;
   uint32_t expect;

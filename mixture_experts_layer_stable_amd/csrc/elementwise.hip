@@ -8,6 +8,7 @@
 //  dwr         dWr[e] = sum over e's routed rows (ascending slot) of dz_s * x_t
 // Each thread owns one 16-byte vector of a row; loops over j / rows run in
 // ascending order with fp32 fused multiply-adds.
+#include "elementwise.h"
 #include "kernels.h"
 
 namespace mok {
@@ -16,47 +17,22 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(Guard gd, const T* __restrict__ part,
                                                       const float* __restrict__ gate, T* __restrict__ y, int64_t T_,
                                                       int H, int k) {
-  constexpr int VE = Elem<T>::VE;
-  const int vpr = H / VE;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (guard_fail(gd) || gid >= T_ * vpr) return;
-  const int64_t t = gid / vpr;
-  const int h0 = (int)(gid - t * vpr) * VE;
-  float acc[VE];
-#pragma unroll
-  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t s = t * k + j;
-    const float g = gate[s];
-    float f[VE];
-    unpack(ldg16(part + s * H + h0), f, (T*)nullptr);
-#pragma unroll
-    for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(g, f[q], acc[q]);
-  }
-  stg16(y + t * H + h0, pack(acc, (T*)nullptr));
+  if (guard_fail(gd)) return;
+  combine_body(part, gate, y, T_, H, k, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// g'_s for the slot of routed row r: the d-gate partials of r's 32-column blocks of I,
-// summed in ascending block order (threads of a wave read consecutive rows: coalesced).
 __global__ __launch_bounds__(256) void router_gsum_kernel(Guard gd, const float* __restrict__ dgp,
                                                           const int32_t* __restrict__ perm,
                                                           float* __restrict__ dgate, int R, int nb) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (guard_fail(gd) || r >= R) return;
-  float v = 0.0f;
-  for (int n = 0; n < nb; ++n) v += dgp[(int64_t)n * R + r];
-  dgate[perm[r]] = v;
+  if (guard_fail(gd)) return;
+  router_gsum_body(dgp, perm, dgate, R, nb, blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// dz_tj = g_tj * (g'_tj - sum_i g_ti g'_ti), the sum in slot order.
 __global__ __launch_bounds__(256) void router_dz_kernel(Guard gd, const float* __restrict__ dgate,
                                                         const float* __restrict__ gate, float* __restrict__ dz,
                                                         int64_t T_, int k) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (guard_fail(gd) || t >= T_) return;
-  float s = 0.0f;
-  for (int j = 0; j < k; ++j) s = __builtin_fmaf(gate[t * k + j], dgate[t * k + j], s);
-  for (int j = 0; j < k; ++j) dz[t * k + j] = gate[t * k + j] * (dgate[t * k + j] - s);
+  if (guard_fail(gd)) return;
+  router_dz_body(dgate, gate, dz, T_, k, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 template <typename T>
@@ -64,103 +40,27 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(Guard gd, const T* __res
                                                         const float* __restrict__ dz, const int32_t* __restrict__ idx,
                                                         const T* __restrict__ wr, T* __restrict__ dx, int64_t T_, int H,
                                                         int k) {
-  constexpr int VE = Elem<T>::VE;
-  const int vpr = H / VE;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (guard_fail(gd) || gid >= T_ * vpr) return;
-  const int64_t t = gid / vpr;
-  const int h0 = (int)(gid - t * vpr) * VE;
-  float acc[VE];
-#pragma unroll
-  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float f[VE];
-    unpack(ldg16(part + (t * k + j) * H + h0), f, (T*)nullptr);
-#pragma unroll
-    for (int q = 0; q < VE; ++q) acc[q] += f[q];
-  }
-  if (wr != nullptr) {
-    for (int j = 0; j < k; ++j) {
-      const float d = dz[t * k + j];
-      float f[VE];
-      unpack(ldg16(wr + (int64_t)idx[t * k + j] * H + h0), f, (T*)nullptr);
-#pragma unroll
-      for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
-    }
-  }
-  stg16(dx + t * H + h0, pack(acc, (T*)nullptr));
+  if (guard_fail(gd)) return;
+  dx_reduce_body(part, dz, idx, wr, dx, T_, H, k, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// dWr[e] = sum over e's routed rows r of dz[perm[r]] * x[token of r]. Workgroup =
-// (expert, block of kDwrVec 16-byte column vectors): thread (row lane l, vector v) sums
-// rows l, l + LANES, l + 2*LANES, ... of the expert in ascending order; then the LANES
-// row-lane sums of each column are added in ascending lane order. The order depends only
-// on H (which picks the shape) and the expert's row count, not on the grid; a hot
-// expert's rows are spread over LANES threads per column. Shapes: 64 lanes x 4 vectors
-// for H <= 2048 (2048 tokens, Zipf: 18 -> 13 us), 32 lanes x 8 vectors (whole 128-byte
-// row pieces) above (Kimi-K2 shape: 0.33 ms, against 0.56 with 64 x 4).
 template <typename T, typename TO, int kDwrVec, int kDwrLanes>
 __global__ __launch_bounds__(kDwrVec * kDwrLanes) void dwr_kernel(Guard gd, const float* __restrict__ dz,
                                                                   const T* __restrict__ x,
                                                                   const int32_t* __restrict__ offsets,
                                                                   const int32_t* __restrict__ perm,
                                                                   TO* __restrict__ dwr, int E, int H, int k) {
-  constexpr int VE = Elem<T>::VE;
-  constexpr int COLS = kDwrVec * VE;
-  __shared__ float red[kDwrLanes][COLS + 1];
+  __shared__ float red[kDwrLanes * (kDwrVec * Elem<T>::VE + 1)];
   if (guard_fail(gd)) return;
-  const int vpr = H / VE;
-  const int nvb = (vpr + kDwrVec - 1) / kDwrVec;
-  const int e = (int)(blockIdx.x / nvb), vb = (int)(blockIdx.x % nvb);
-  const int tv = threadIdx.x % kDwrVec, rl = threadIdx.x / kDwrVec;
-  const int v = vb * kDwrVec + tv;
-  float acc[VE];
-#pragma unroll
-  for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
-  if (v < vpr) {
-    const int r1 = offsets[e + 1];
-    for (int r = offsets[e] + rl; r < r1; r += kDwrLanes) {
-      const int s = perm[r];
-      const float d = dz[s];
-      float f[VE];
-      unpack(ldg16(x + (int64_t)(s / k) * H + v * VE), f, (T*)nullptr);
-#pragma unroll
-      for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < VE; ++q) red[rl][tv * VE + q] = acc[q];
-  __syncthreads();
-  if (threadIdx.x < COLS) {
-    const int col = (int)threadIdx.x;
-    float sum = 0.0f;
-#pragma unroll 8
-    for (int l = 0; l < kDwrLanes; ++l) sum += red[l][col];
-    if (vb * kDwrVec + col / VE < vpr) Elem<TO>::put(dwr + (int64_t)e * H, (int64_t)vb * COLS + col, sum);
-  }
+  dwr_body<T, TO, kDwrVec, kDwrLanes>(dz, x, offsets, perm, dwr, E, H, k, (int)blockIdx.x, red);
 }
 
-// dst[r] = src[perm[r] / k] (* gate[perm[r]], rounded to bf16): token rows in routed order.
 __global__ __launch_bounds__(256) void gather_rows_kernel(Guard gd, const bf16* __restrict__ src,
                                                           const int32_t* __restrict__ perm,
                                                           const float* __restrict__ gate, bf16* __restrict__ dst, int R,
                                                           int H, int k) {
-  const int vpr = H / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (guard_fail(gd) || gid >= (int64_t)R * vpr) return;
-  const int r = (int)(gid / vpr);
-  const int h0 = (int)(gid - (int64_t)r * vpr) * 8;
-  const int s = perm[r];
-  uint4 v = ldg16(src + (int64_t)(s / k) * H + h0);
-  if (gate != nullptr) {
-    const float g = gate[s];
-    float f[8];
-    unpack(v, f, (bf16*)nullptr);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) f[q] = g * f[q];
-    v = pack(f, (bf16*)nullptr);
-  }
-  stg16(dst + (int64_t)r * H + h0, v);
+  if (guard_fail(gd)) return;
+  gather_rows_body(src, perm, gate, dst, R, H, k, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }

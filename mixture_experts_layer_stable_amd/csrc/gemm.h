@@ -277,13 +277,16 @@ struct RowTile {
   int e, m, n, row0, nrows;
 };
 
+// wg / nwg: this workgroup's index and the number of workgroups walking the tiles (the
+// grid of a kernel of its own, or of a fused persistent kernel).
 template <class F>
-__device__ __forceinline__ void for_each_row_tile(const Sched& sc, const int* s_ts, int NTN, F&& body) {
+__device__ __forceinline__ void for_each_row_tile(const Sched& sc, const int* s_ts, int NTN, int wg, int nwg,
+                                                  F&& body) {
   const int64_t total = (int64_t)s_ts[sc.E] * NTN;
-  const int P = min(8, (int)gridDim.x);  // partitions (XCDs that have workgroups)
-  const int xcd = blockIdx.x % P;
-  const int nx = ((int)gridDim.x - xcd + P - 1) / P;
-  const int li = blockIdx.x / P;
+  const int P = min(8, nwg);  // partitions (XCDs that have workgroups)
+  const int xcd = wg % P;
+  const int nx = (nwg - xcd + P - 1) / P;
+  const int li = wg / P;
   const int64_t lo = total * xcd / P, hi = total * (xcd + 1) / P;
   for (int64_t L = lo + li; L < hi; L += nx) {
     // e = last expert with s_ts[e] * NTN <= L

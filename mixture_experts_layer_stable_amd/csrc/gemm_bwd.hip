@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs<T> a) {
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
   load_tile_start(a.sc, s_ts);
-  for_each_row_tile(a.sc, s_ts, a.I / Tl::BN, [&](const RowTile& t) {
+  for_each_row_tile(a.sc, s_ts, a.I / Tl::BN, blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
     for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs<T> a) {
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
   load_tile_start(a.sc, s_ts);
-  for_each_row_tile(a.sc, s_ts, a.H / Tl::BN, [&](const RowTile& t) {
+  for_each_row_tile(a.sc, s_ts, a.H / Tl::BN, blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
     for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();

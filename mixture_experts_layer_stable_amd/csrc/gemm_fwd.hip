@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<T> a) {
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int I2 = 2 * a.I;
   load_tile_start(a.sc, s_ts);
-  for_each_row_tile(a.sc, s_ts, a.I / (Tl::BN / 2), [&](const RowTile& t) {
+  for_each_row_tile(a.sc, s_ts, a.I / (Tl::BN / 2), blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
     for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args<T> a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   load_tile_start(a.sc, s_ts);
-  for_each_row_tile(a.sc, s_ts, a.H / Tl::BN, [&](const RowTile& t) {
+  for_each_row_tile(a.sc, s_ts, a.H / Tl::BN, blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
     for (int i = tid; i < Tl::BM; i += kThreads) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
   const int K = KIND == MFC1 || KIND == MDH ? a.H : (KIND == MFC2 ? a.I : I2);
   const int KB = K / 32;  // scale bytes per row
   load_tile_start(a.sc, s_ts);
-  for_each_row_tile(a.sc, s_ts, N / Tl::BN, [&](const RowTile& t) {
+  for_each_row_tile(a.sc, s_ts, N / Tl::BN, blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
     for (int i = tid; i < Tl::BM; i += Tl::NT) s_slot[i] = i < t.nrows ? a.sc.perm[t.row0 + i] : -1;
     __syncthreads();

@@ -95,6 +95,16 @@ hipError_t launch_dw_mx(const Ctx& c, const int32_t* pofs, const void* aq, const
 // by the schedule's scratch sizing and its launches.
 inline int sched_block(int64_t R) { return R <= 65536 ? 1024 : 4096; }
 
+// Fused forward (fc1 -> fc2 -> combine) and backward (dh + row gathers -> router backward ->
+// dx + weight gradients + dWr -> dx reduction): one cooperative persistent launch each,
+// stages separated by a grid barrier. bf16, 32-row schedule tiles.
+hipError_t launch_forward_fused(const Ctx& c, const void* x, const void* w1, const void* w2, void* au, void* h,
+                                void* part, const float* gate, void* y);
+hipError_t launch_backward_fused(const Ctx& c, const void* x, const int32_t* idx, const float* gate, const void* w1,
+                                 const void* w2, const void* wr, const void* au, const void* h, const void* dy,
+                                 void* dgu, void* bpart, float* dgp, float* dz, void* xs, void* dos, void* dx,
+                                 void* dw1, void* dw2, float* dgate, void* dwr);
+
 // Tile widths (N) of the row GEMMs; shared by workspace sizing and launches.
 inline int bn_fc1(int I) { return I % 128 == 0 ? 256 : 128; }
 inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }
@@ -102,6 +112,8 @@ inline int bn_rows(int N) { return N % 256 == 0 ? 256 : 128; }
 inline int bn_rows_bf16(int N, int BM) { return (BM == 128 && N % 512 == 0) ? 512 : bn_rows(N); }
 // d-gate partials per routed row: one per 32-column block of I (summed in ascending
 // block order by router_bwd, so the bits do not depend on the GEMM's tiling)
-inline int dgate_parts(int I) { return I / 32; }
+__host__ __device__ inline int dgate_parts(int I) { return I / 32; }
+// The fused backward keeps one token's d-gate partials (k * I/32 floats) in LDS.
+constexpr int kFusedMaxSlotParts = 2048;
 
 }  // namespace mok

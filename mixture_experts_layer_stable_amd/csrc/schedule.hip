@@ -34,6 +34,7 @@ __device__ __forceinline__ void stamp_header(const Stamp& st) {
   st.hdr[2] = st.tile_m;
   st.hdr[3] = st.max_tiles;
   st.hdr[kHdrStatus] = MOK_OK;
+  sync_zero(st.hdr);
 }
 
 constexpr int kSchedWaves = 16;  // waves of the scatter block

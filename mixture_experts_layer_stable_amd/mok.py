@@ -21,6 +21,7 @@ F32, BF16, MXFP8 = 0, 1, 2
 FLAG_WGRAD_F32 = 1
 FLAG_WGRAD_DEFER = 2
 FLAG_REPLAY = 4
+FLAG_FUSED = 8
 DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8}
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 

@@ -38,12 +38,13 @@ class Case:
 
 
 def run_gpu(case: Case, backward=True, tile_m=0, grid=0, router_grad=True, wgrad_f32=False, logits=True,
-            replay=False):
+            replay=False, fused=False):
     from mixture_experts_layer_stable_amd import mok
     w = case.w
     dev = "cuda"
     d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.DTYPES[w.act], tile_m=tile_m, grid=grid,
-                 flags=(mok.FLAG_WGRAD_F32 if wgrad_f32 else 0) | (mok.FLAG_REPLAY if replay else 0))
+                 flags=(mok.FLAG_WGRAD_F32 if wgrad_f32 else 0) | (mok.FLAG_REPLAY if replay else 0)
+                 | (mok.FLAG_FUSED if fused else 0))
     buf = mok.Buffers(d, dev, backward=backward, wgrad_f32=wgrad_f32)
     x = case.x.to(dev)
     wr = case.wr.to(dev)

@@ -266,3 +266,60 @@ def test_replay_bit_identical(name, kw):
         a, b = got[key], ref[key]
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b), key
+
+
+def _same(got, ref, keys):
+    for key in keys:
+        a, b = got[key], ref[key]
+        if isinstance(a, np.ndarray):
+            np.testing.assert_array_equal(a, b, err_msg=key)
+        else:
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), key
+
+
+@pytest.mark.parametrize("name,kw,grid", [("small_bf16", {}, 0), ("imbalanced_bf16", {}, 0),
+                                          ("small_bf16", dict(T=300, E=12, k=3, H=256, I=128), 7),
+                                          ("small_bf16", dict(T=256, E=16, k=2, H=4096, I=128), 0),
+                                          ("small_bf16", dict(T=200, E=8, k=2, H=384, I=384), 300)])
+def test_fused_persistent_kernels_bit_identical(name, kw, grid):
+    """MOK_FLAG_FUSED: the forward and the backward each as one cooperative persistent launch
+    with grid barriers between the stages; every output equals the separate kernels' bits
+    (also with 7 workgroups and with a grid request above the compute-unit count, H = 4096
+    and H, I not multiples of 256), and the oracle agrees within the bf16 tolerance."""
+    w = _w(name, **kw)
+    print("case fused", w, "grid", grid, flush=True)
+    case = Case(w)
+    ref = run_gpu(case)
+    got = run_gpu(case, fused=True, grid=grid)
+    assert got["tile_m"] == 32
+    _same(got, ref, ("idx", "gate", "perm", "dgate", "y", "a", "u", "h", "dx", "dw1", "dw2", "dwr"))
+    o = run_oracle(case, BM=32)
+    _check_forward(w, got, o, TOL["bf16"])
+    _check_backward(w, got, o, TOL["bf16"])
+
+
+def test_fused_replay_and_no_router_backward():
+    """Fused kernels with activation replay (a separate FC1 launch before the fused backward)
+    and with the router backward skipped (wr = dwr = NULL)."""
+    w = _w("small_bf16", T=512, E=16)
+    case = Case(w)
+    _same(run_gpu(case, fused=True, replay=True), run_gpu(case), ("y", "dx", "dw1", "dw2", "dwr", "dgate"))
+    _same(run_gpu(case, fused=True, router_grad=False), run_gpu(case, router_grad=False),
+          ("y", "dx", "dw1", "dw2", "dgate"))
+
+
+def test_fused_needs_bf16_and_32_row_tiles():
+    from mixture_experts_layer_stable_amd import mok
+    w = _w("small_bf16", T=256, E=8, H=256, I=256)
+    case = Case(w)
+    with pytest.raises(mok.MokError) as ei:
+        run_gpu(case, fused=True, tile_m=64)
+    assert ei.value.status == 3
+    with pytest.raises(mok.MokError) as ei:
+        run_gpu(Case(_w("tiny_fp32", backward=True)), fused=True)
+    assert ei.value.status == 4
+    # k * I/32 = 4096 d-gate partials per token exceed what one workgroup keeps in LDS
+    with pytest.raises(mok.MokError) as ei:
+        run_gpu(Case(_w("small_bf16", T=64, E=16, k=16, H=128, I=8192)), fused=True, tile_m=32)
+    assert ei.value.status == 3
