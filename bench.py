@@ -12,7 +12,8 @@ With --config kimi_k2_mxfp8_stream a step is the streamed MXFP8 step: 8 micro-ba
 of 2048 tokens (route, schedule, forward for 0..7, then backward for 7..0 through a
 2-slot ring, weight gradients deferred to the last call). The expert weights are
 quantised to their four MXFP8 orientations once, before timing (a per-weight-update
-cost); activation and gradient quantisation is inside the step.
+cost); activation and gradient quantisation is inside the step. --gemm mxfp4 runs the
+same streamed step with MXFP4 (E2M1) expert GEMMs.
 
 Prints one JSON line. Runs on one GPU only; --gpus N > 1 exits with a message.
 """
@@ -28,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; grouped-GEMM MFMA util %"
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "mxfp4": 10100.0}
+MX_ELEM_BYTES = {"mxfp8": 1.0 + 1.0 / 32.0, "mxfp4": 0.5 + 1.0 / 32.0}  # element + its share of the scale byte
 HBM_PEAK_GBS = 8000.0
 GEMMS = ("fc1", "fc2", "dh", "dx", "dw2", "dw1")
 FUSED = ("forward_fused", "backward_fused")  # whole passes in one persistent launch (their GEMMs and the rest)
@@ -36,10 +38,12 @@ FUSED = ("forward_fused", "backward_fused")  # whole passes in one persistent la
 # dense MFMA peak and the compulsory HBM bytes (weights once per pass, or once per
 # micro-batch when streamed; activations once) at 8 TB/s. 2048-token bf16 steps: 0.46 GB
 # -> 0.058 ms; Kimi-K2 bf16: 34.6 TFLOP (13.9 ms) against 121 GB (15.1 ms); streamed
-# MXFP8: 328 GB of weight re-reads and activations -> 41 ms. The 64-token fp32 step is
-# bound by launch latency and has none.
+# MXFP8: 328 GB of weight re-reads and activations -> 41 ms; the same step with MXFP4
+# weights: the 245 GB of E4M3 weight re-reads become 245 * (0.5 + 1/32) / (1 + 1/32) =
+# 126 GB, the other 83 GB stay -> 209 GB, 26.2 ms. The 64-token fp32 step is bound by
+# launch latency and has none.
 STEP_ROOFLINE_MS = {"small_bf16": 0.058, "imbalanced_bf16": 0.058, "kimi_k2_bf16": 15.1,
-                    "kimi_k2_mxfp8_stream": 41.0}
+                    "kimi_k2_mxfp8_stream": 41.0, "kimi_k2_mxfp8_stream/mxfp4": 26.2}
 
 
 def launch_flops(w, name):
@@ -68,8 +72,8 @@ def kernel_work(w, name, active_experts=None):
     R = T * w.k
     es = 4 if w.act == "f32" else 2
     flops = {k: launch_flops(w, k) for k in GEMMS + FUSED}
-    if w.gemm == "mxfp8" and name in ("fc1", "fc2", "dh", "dx"):
-        q = 33.0 / 32.0  # E4M3 byte + one scale byte per 32
+    if w.gemm in MX_ELEM_BYTES and name in ("fc1", "fc2", "dh", "dx"):
+        q = MX_ELEM_BYTES[w.gemm]
         ae = E if active_experts is None else active_experts
         wbytes = {"fc1": 2 * I * H, "fc2": H * I, "dh": I * H, "dx": H * 2 * I}[name] * q * ae
         act = {"fc1": T * H * q + R * (2 * I * 2 + I * 2 + I * q),
@@ -77,7 +81,7 @@ def kernel_work(w, name, active_experts=None):
                "dh": T * H * q + R * (2 * I * 2 + I * 2 + 4) + R * (2 * I * 2 + 2 * I * q),
                "dx": R * 2 * I * q + R * H * 2}[name]
         b = wbytes + act
-        if b / (HBM_PEAK_GBS * 1e9) > flops[name] / (MFMA_PEAK_TFLOPS["mxfp8"] * 1e12):
+        if b / (HBM_PEAK_GBS * 1e9) > flops[name] / (MFMA_PEAK_TFLOPS[w.gemm] * 1e12):
             return "hbm", b
         return "mfma", flops[name]
     if name in flops:
@@ -173,9 +177,10 @@ def cpu_baseline(w, ntok, kept):
     W = KeptWeights(kept)
     t0 = time.perf_counter()
     _, idx, g = oracle.route(x, wr, w.k, b)
-    if w.gemm == "mxfp8":
-        fwd = oracle.mx.forward_mx(x, W, idx, g, w.E, w.I)
-        oracle.mx.backward_mx(x, W, wr, idx, g, fwd, dy, w.I)
+    if w.gemm in ("mxfp8", "mxfp4"):
+        fmt = "e2m1" if w.gemm == "mxfp4" else "e4m3"
+        fwd = oracle.mx.forward_mx(x, W, idx, g, w.E, w.I, fmt=fmt)
+        oracle.mx.backward_mx(x, W, wr, idx, g, fwd, dy, w.I, fmt=fmt)
     else:
         fwd = oracle.forward(x, W, idx, g, w.act, w.E, w.I)
         oracle.backward(x, W, wr, idx, g, fwd, dy, w.act, w.I)
@@ -210,6 +215,8 @@ def main():
                     help="one persistent launch per pass (bf16, 32-row schedule tiles)")
     ap.add_argument("--replay", action="store_true",
                     help="forward-activation replay: keep no activations, form them again in the backward")
+    ap.add_argument("--gemm", choices=["mxfp8", "mxfp4"], default=None,
+                    help="element format of the MX expert GEMMs of an MX workload (default: the workload's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (known bytes, for HBM counter scaling)")
     args = ap.parse_args()
@@ -222,7 +229,12 @@ def main():
     from mixture_experts_layer_stable_amd import inputs, mok
 
     w = inputs.WORKLOADS[args.config]
-    mx = w.gemm == "mxfp8"
+    if args.gemm is not None:
+        if w.gemm not in ("mxfp8", "mxfp4"):
+            print("--gemm applies to the MX workloads only", file=sys.stderr)
+            sys.exit(2)
+        w = inputs.replace(w, gemm=args.gemm)
+    mx = w.gemm in ("mxfp8", "mxfp4")
     torch.cuda.set_device(0)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.calibrate_copy:
@@ -242,7 +254,7 @@ def main():
 
     if mx:
         M = w.micro_batches
-        d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=args.tile_m, mb_count=M,
+        d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.DTYPES[w.gemm], tile_m=args.tile_m, mb_count=M,
                      ring=2, flags=mok.FLAG_REPLAY if args.replay else 0)
         q = mok.MxWeights(d, "cuda")
         mok.weights_quantize(d, w1, w2, q)
@@ -304,7 +316,8 @@ def main():
         peak = HBM_PEAK_GBS
         achieved = work / (dom_ms * 1e-3) / 1e9
         unit = "GB/s"
-    traffic = measured_traffic(dominant, w.name)
+    traffic = measured_traffic(dominant, w.name) if args.gemm in (None, "mxfp8") else None
+    rkey = w.name if args.gemm in (None, "mxfp8") else "%s/%s" % (w.name, args.gemm)
     gemm_ms = sum(per.get(k, 0.0) for k in GEMMS + FUSED)
     gemm_flops = sum(launches_per_step(w, k) * launch_flops(w, k) for k in GEMMS)
     mfma_util = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (MFMA_PEAK_TFLOPS[gdt] * 1e12) if gemm_ms else None
@@ -326,12 +339,12 @@ def main():
                    "routing": "zipf-imbalanced" if w.zipf else "near-uniform", "tile_m": d.c().tile_m or "auto",
                    **({"activations": "replayed"} if args.replay else {}),
                    **({"launches": "one persistent kernel per pass"} if args.fused else {}),
-                   **({"micro_batches": w.micro_batches, "ring_slots": 2} if mx else {})},
+                   **({"micro_batches": w.micro_batches, "ring_slots": 2, "gemm": w.gemm} if mx else {})},
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},
         "gemm_mfma_util_pct": mfma_util,
-        "step_roofline": ({"ms": STEP_ROOFLINE_MS[w.name], "tokens_per_s": w.T / (STEP_ROOFLINE_MS[w.name] * 1e-3),
-                           "frac": STEP_ROOFLINE_MS[w.name] / ms_step} if w.name in STEP_ROOFLINE_MS else None),
+        "step_roofline": ({"ms": STEP_ROOFLINE_MS[rkey], "tokens_per_s": w.T / (STEP_ROOFLINE_MS[rkey] * 1e-3),
+                           "frac": STEP_ROOFLINE_MS[rkey] / ms_step} if rkey in STEP_ROOFLINE_MS else None),
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
     }
 
@@ -342,7 +355,7 @@ def main():
         result["cpu_baseline"] = {
             "value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": "first %d of %d tokens (%d routed rows): oracle%s route + forward + backward, %.1f s" % (
-                ntok, w.T, rows, " MXFP8" if mx else "", dt)}
+                ntok, w.T, rows, " " + w.gemm.upper() if mx else "", dt)}
     print(json.dumps(result), flush=True)
 
 

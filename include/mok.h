@@ -43,6 +43,12 @@
  *    the routed rows of one expert in blocks of 32 from its first row of the
  *    whole step (all micro-batches, in token order), the last block zero-padded.
  *    Quantiser inputs are the stored bf16 values; outputs are stored as with bf16.
+ *    MOK_MXFP4 (with act = MOK_BF16; the narrower expert GEMMs of aikraft.ru MoK
+ *    article, section 03): the same quantisation points and scales with FP4 E2M1
+ *    elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; round to
+ *    nearest even, saturating at +-6; s = floor(log2 amax) - 2), two elements per
+ *    byte with the even element in the low nibble (sign bit 3, exponent bits 2..1,
+ *    mantissa bit 0).  Needs H and I multiples of 256.
  *  - Layouts: x, y, dy, dx [T][H]; wr [E][H]; w1 [E][2I][H] (rows 0..I-1 are
  *    the SwiGLU gate projection, rows I..2I-1 the up projection); w2 [E][H][I];
  *    idx [T][k] int32; gate, dgate, logits [T][k] / [T][E] fp32.
@@ -84,7 +90,7 @@ typedef enum mok_status {
                                     in the schedule header's status word, see above) */
 } mok_status;
 
-typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
+typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2, MOK_MXFP4 = 3 } mok_dtype;
 
 /* flags */
 #define MOK_FLAG_WGRAD_F32 1u   /* dw1, dw2, dwr are written as fp32 instead of `act` */
@@ -118,20 +124,22 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2 } mok_dtype;
 /*
  * Problem descriptor.  Limits: T >= 0; 1 <= k <= min(E, 16); 1 <= E <= 1024;
  * H and I positive multiples of 128; T*k, T*H, T*k*2I and 2I*H below 2^31.
- * act is MOK_F32 or MOK_BF16; gemm equals act, or is MOK_MXFP8 with act = MOK_BF16
- * (anything else: MOK_ERR_DTYPE).
+ * act is MOK_F32 or MOK_BF16; gemm equals act, or is MOK_MXFP8 or MOK_MXFP4 with
+ * act = MOK_BF16 (anything else: MOK_ERR_DTYPE); MOK_MXFP4 needs H and I multiples
+ * of 256 (else MOK_ERR_SHAPE).
  * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile
  *   that still gives every grouped GEMM at least two full waves of the
  *   GPU's compute units.
  * grid: workgroups of the persistent GEMM kernels; 0 = one wave of the GPU.
- * Micro-batch streaming (MXFP8 only; bf16/fp32 need mb_count <= 1): one step is
+ * Micro-batch streaming (MX only; bf16/fp32 need mb_count <= 1): one step is
  *   mb_count micro-batches of T tokens each, forward in any order and backward in
  *   any order, every call naming its micro-batch in mb_index (0 <= mb_index <
  *   mb_count).  ring: number of slots of the forward and backward workspaces
  *   (the fixed ring that the pages' rotating token buffer becomes on one GPU);
  *   micro-batch m uses slot m % ring, so calls for micro-batches in the same slot
  *   must not overlap in time (one stream orders them).  mb_count = 0 and ring = 0
- *   mean 1.  Extra limit for MXFP8: (mb_count*T*k + 128*E) * max(H, 2I) < 2^31.
+ *   mean 1.  Extra limit for MX: (mb_count*T*k + 256*E) * max(H, 2I) < 2^31
+ *   (128*E for MXFP8).
  * The same descriptor must be passed to mok_schedule_build and to the
  * forward/backward calls that use that schedule (mb_index may differ).
  */
@@ -149,8 +157,9 @@ typedef struct mok_desc {
   int32_t reserved; /* must be 0 */
 } mok_desc;
 
-/* MXFP8 expert weights, quantised once per weight update by mok_weights_quantize.
- * Each orientation is K-contiguous for the GEMM that reads it; *q are E4M3 bytes,
+/* MX expert weights, quantised once per weight update by mok_weights_quantize.
+ * Each orientation is K-contiguous for the GEMM that reads it; *q are E4M3 bytes
+ * (MXFP8) or E2M1 codes two per byte (MXFP4: the *q shapes below with K halved),
  * *s the E8M0 scale bytes of consecutive 32-element blocks along K, stored
  * K-tile-major: for every 128-element K-tile, the 4 scale bytes of each row, rows
  * consecutive, so a GEMM tile's scales for one K-tile are one contiguous run.
@@ -164,11 +173,11 @@ typedef struct mok_mx_weights {
 } mok_mx_weights;
 
 /* Expert weights (device pointers).  w1, w2 in `act`; mx (read only by the
- * forward and backward calls) is required when gemm = MOK_MXFP8, else ignored. */
+ * forward and backward calls) is required when gemm is MX, else ignored. */
 typedef struct mok_weights {
   const void* w1;            /* [E][2I][H] */
   const void* w2;            /* [E][H][I]  */
-  const mok_mx_weights* mx;  /* host pointer to the MXFP8 orientations, or NULL */
+  const mok_mx_weights* mx;  /* host pointer to the MX orientations, or NULL */
 } mok_weights;
 
 /* Sizes in bytes of the caller-owned buffers (worst case over routings). */
@@ -240,7 +249,7 @@ typedef struct mok_mx_layout {
 mok_status mok_workspace_query(const mok_desc* d, mok_sizes* sizes);
 mok_status mok_schedule_layout_query(const mok_desc* d, mok_schedule_layout* layout);
 mok_status mok_saved_layout_query(const mok_desc* d, mok_saved_layout* layout);
-/* MOK_ERR_DTYPE unless gemm = MOK_MXFP8. */
+/* MOK_ERR_DTYPE unless gemm is MOK_MXFP8 or MOK_MXFP4. */
 mok_status mok_mx_layout_query(const mok_desc* d, mok_mx_layout* layout);
 
 /*
@@ -320,7 +329,7 @@ mok_status mok_moe_forward_noalloc(const mok_desc* d, void* sched, const void* x
  * holds only the expert term.  dgate [T][k] fp32 receives g'.  Every element
  * of dw1 [E][2I][H], dw2 [E][H][I], dwr [E][H] is written (zero for experts
  * without tokens).  ws has mok_sizes.bwd_ws bytes.
- * MXFP8 (gemm = MOK_MXFP8): dY rows are quantised along H and dGU rows along 2I
+ * MX (gemm = MOK_MXFP8 or MOK_MXFP4): dY rows are quantised along H and dGU rows along 2I
  * inside the call (dGU in the dh epilogue); w->mx supplies w2tq/w2ts and
  * w1tq/w1ts.  The weight gradients are deferred: every call copies micro-batch
  * mb_index's routed-order x, dO = g*dy (rounded to bf16), h and dGU rows, its dz
@@ -365,11 +374,11 @@ typedef struct mok_trace {
  * range, MOK_ERR_NULL if filter or events is NULL. */
 mok_status mok_trace_bind(mok_trace* t);
 /*
- * mok_weights_quantize -- the MXFP8 orientations of bf16 expert weights w1
+ * mok_weights_quantize -- the MX orientations of bf16 expert weights w1
  * [E][2I][H] and w2 [E][H][I] (see mok_mx_weights for shapes): w1q/w2q quantise
  * rows along their contiguous axis; w2tq[e][i][h] and w1tq[e][h][c] are W2[e][h][i]
  * and W1[e][c][h] quantised in blocks of 32 along h and c respectively and stored
- * transposed.  Requires act = MOK_BF16 and gemm = MOK_MXFP8; every pointer in
+ * transposed.  Requires act = MOK_BF16 and gemm = MOK_MXFP8 or MOK_MXFP4; every pointer in
  * *out non-NULL and 16-byte aligned.  Run once per weight update, outside the
  * layer step.
  */

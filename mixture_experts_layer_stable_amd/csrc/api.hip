@@ -17,7 +17,9 @@ int elem_size(int act) { return act == MOK_F32 ? 4 : 2; }
 
 int mb_count_of(const mok_desc* d) { return d->mb_count > 0 ? d->mb_count : 1; }
 int ring_of(const mok_desc* d) { return d->ring > 0 ? d->ring : 1; }
-bool is_mx(const mok_desc* d) { return d->gemm == MOK_MXFP8; }
+bool is_mx(const mok_desc* d) { return d->gemm == MOK_MXFP8 || d->gemm == MOK_MXFP4; }
+// Quantised element bytes of n MX elements (E4M3: 1 each; E2M1: two per byte).
+size_t mxb(const mok_desc* d, int64_t n) { return (size_t)(d->gemm == MOK_MXFP4 ? n / 2 : n); }
 bool is_replay(const mok_desc* d) { return (d->flags & MOK_FLAG_REPLAY) != 0; }
 bool is_fused(const mok_desc* d) { return (d->flags & MOK_FLAG_FUSED) != 0; }
 
@@ -29,16 +31,17 @@ mok_status check_fused(const mok_desc* d, const Ctx& c) {
   return MOK_OK;
 }
 
-// Rows of the token-axis operands of the MXFP8 weight-gradient GEMMs: every
-// expert's rows of the step padded to a multiple of 128.
+// Rows of the token-axis operands of the MX weight-gradient GEMMs: every expert's rows
+// of the step padded to a whole K-tile (128 elements for MXFP8, 256 for MXFP4).
 int64_t mx_kmax(const mok_desc* d) {
-  return ((int64_t)mb_count_of(d) * d->T * d->k + 128LL * d->E + 127) / 128 * 128;
+  const int64_t kt = d->gemm == MOK_MXFP4 ? 256 : 128;
+  return ((int64_t)mb_count_of(d) * d->T * d->k + kt * d->E + kt - 1) / kt * kt;
 }
 
 mok_status check_desc(const mok_desc* d) {
   if (d == nullptr) return MOK_ERR_NULL;
   if (d->act != MOK_F32 && d->act != MOK_BF16) return MOK_ERR_DTYPE;
-  if (d->gemm != d->act && !(d->gemm == MOK_MXFP8 && d->act == MOK_BF16)) return MOK_ERR_DTYPE;
+  if (d->gemm != d->act && !(is_mx(d) && d->act == MOK_BF16)) return MOK_ERR_DTYPE;
   if ((d->flags & MOK_FLAG_WGRAD_DEFER) && !is_mx(d)) return MOK_ERR_DTYPE;
   if (d->reserved != 0 || d->mb_count < 0 || d->ring < 0 || d->mb_count > 1024 || d->ring > 1024)
     return MOK_ERR_SHAPE;
@@ -46,6 +49,8 @@ mok_status check_desc(const mok_desc* d) {
   if (!is_mx(d) && mb_count_of(d) > 1) return MOK_ERR_SHAPE;
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > 16 || d->k > d->E) return MOK_ERR_SHAPE;
   if (d->H <= 0 || d->I <= 0 || d->H % 128 != 0 || d->I % 128 != 0) return MOK_ERR_SHAPE;
+  // MXFP4 K-tiles are 256 elements along H, I and 2I
+  if (d->gemm == MOK_MXFP4 && (d->H % 256 != 0 || d->I % 256 != 0)) return MOK_ERR_SHAPE;
   if (d->T * (int64_t)d->k >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
   // 32-bit byte offsets inside one operand: token rows, routed rows, one expert's weights
   if (d->T * (int64_t)d->H >= ((int64_t)1 << 31)) return MOK_ERR_SHAPE;
@@ -143,7 +148,8 @@ Layout layout_of(const mok_desc* d, int BM) {
   return L;
 }
 
-// MXFP8 buffer layout. Forward ring slot: quantised x rows, quantised h rows, partial
+// MX buffer layout (quantised rows hold 1 byte per element for MXFP8, half for MXFP4;
+// scales 1 byte per 32 elements). Forward ring slot: quantised x rows, quantised h rows, partial
 // rows. Backward ring slot: quantised dY and dGU rows, partial rows, d-gate parts.
 // Then the stash of all micro-batches (array-major: micro-batch m's part of each
 // array at its m-th R rows) and the flush buffers.
@@ -160,9 +166,9 @@ MxLayout mx_layout_of(const mok_desc* d) {
   const int64_t T = d->T, R = d->T * d->k, H = d->H, I = d->I, E = d->E;
   const int64_t M = mb_count_of(d), S = ring_of(d);
   size_t o = 0;
-  L.xq = o; o = up(o + (size_t)(T * H));
+  L.xq = o; o = up(o + mxb(d, T * H));
   L.xs = o; o = up(o + (size_t)(T * H / 32));
-  L.hq = o; o = up(o + (size_t)(R * I));
+  L.hq = o; o = up(o + mxb(d, R * I));
   L.hs = o; o = up(o + (size_t)(R * I / 32));
   L.part = o; o = up(o + (size_t)(2 * R * H));
   // replay: a|u and h of this micro-batch live in the slot instead of `saved`
@@ -172,16 +178,16 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.fslot = o;
   L.fwd = (size_t)S * L.fslot;
   o = 0;
-  L.dyq = o; o = up(o + (size_t)(T * H));
+  L.dyq = o; o = up(o + mxb(d, T * H));
   L.dys = o; o = up(o + (size_t)(T * H / 32));
-  L.dguq = o; o = up(o + (size_t)(R * 2 * I));
+  L.dguq = o; o = up(o + mxb(d, R * 2 * I));
   L.dgus = o; o = up(o + (size_t)(R * 2 * I / 32));
   L.bpart = o; o = up(o + (size_t)(2 * R * H));
   L.dgp = o; o = up(o + (size_t)(4 * R * dgate_parts(d->I)));
   // replay: the backward forms quantised x, a|u, h (and quantised h) again in its slot
-  L.bxq = o; o = up(o + rp * (size_t)(T * H));
+  L.bxq = o; o = up(o + rp * mxb(d, T * H));
   L.bxs = o; o = up(o + rp * (size_t)(T * H / 32));
-  L.bhq = o; o = up(o + rp * (size_t)(R * I));
+  L.bhq = o; o = up(o + rp * mxb(d, R * I));
   L.bhs = o; o = up(o + rp * (size_t)(R * I / 32));
   L.bau = o; o = up(o + rp * (size_t)(2 * R * 2 * I));
   L.bh = o; o = up(o + rp * (size_t)(2 * R * I));
@@ -200,13 +206,13 @@ MxLayout mx_layout_of(const mok_desc* d) {
   L.gcnt = o; o = up(o + (size_t)(4 * E));
   L.pofs = o; o = up(o + (size_t)(4 * (E + 1)));
   L.rowmap = o; o = up(o + (size_t)(4 * K));
-  L.xt = o; o = up(o + (size_t)(H * K));
+  L.xt = o; o = up(o + mxb(d, H * K));
   L.xts = o; o = up(o + (size_t)(H * K / 32));
-  L.dot = o; o = up(o + (size_t)(H * K));
+  L.dot = o; o = up(o + mxb(d, H * K));
   L.dots = o; o = up(o + (size_t)(H * K / 32));
-  L.ht = o; o = up(o + (size_t)(I * K));
+  L.ht = o; o = up(o + mxb(d, I * K));
   L.hts = o; o = up(o + (size_t)(I * K / 32));
-  L.dgut = o; o = up(o + (size_t)(2 * I * K));
+  L.dgut = o; o = up(o + mxb(d, 2 * I * K));
   L.dguts = o; o = up(o + (size_t)(2 * I * K / 32));
   L.dwrp = o; o = up(o + dwr_stash_part_bytes((int)E, (int)H));
   L.bwd = o;
@@ -258,6 +264,7 @@ mok_status make_ctx(const mok_desc* d, const void* sched, void* stream, Ctx* c) 
   c->num_cu = cus;
   c->grid = d->grid;
   c->gemm = d->gemm;
+  c->mx4 = d->gemm == MOK_MXFP4;
   c->s = (hipStream_t)stream;
   c->counts = (int32_t*)(sb + L.counts);
   c->offsets = (int32_t*)(sb + L.offsets);
@@ -325,7 +332,7 @@ bool trace_on(const char* name) {
     }                                                                                           \
   } while (0)
 
-// MXFP8 backward of micro-batch d->mb_index (see mok_moe_backward in mok.h).
+// MX backward of micro-batch d->mb_index (see mok_moe_backward in mok.h).
 mok_status mx_backward(const mok_desc* d, const Ctx& c, const void* x, const int32_t* idx, const float* gate,
                        const mok_weights* w, const void* wr, const void* saved, const void* dy, void* dx, void* dw1,
                        void* dw2, float* dgate, void* dwr, void* ws) {
@@ -666,6 +673,7 @@ mok_status mok_weights_quantize(const mok_desc* d, const void* w1, const void* w
   c.E = d->E;
   c.H = d->H;
   c.I = d->I;
+  c.mx4 = d->gemm == MOK_MXFP4;
   c.s = (hipStream_t)stream;
   const int64_t E = d->E, H = d->H, I = d->I;
   MOK_LAUNCH("quant", c.s, launch_mx_quant_rows(c, w1, E * 2 * I, (int)H, out->w1q, out->w1s, 2 * I));
@@ -702,6 +710,6 @@ const char* mok_status_string(mok_status s) {
   return "unknown status";
 }
 
-int32_t mok_version(void) { return 300; }
+int32_t mok_version(void) { return 301; }
 
 }  // extern "C"

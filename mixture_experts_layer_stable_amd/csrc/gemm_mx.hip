@@ -1,7 +1,8 @@
-// MXFP8 grouped expert GEMMs: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 x E4M3
-// operands, one E8M0 scale per 32 K-elements of every row of A and B, fp32
-// accumulation (expert GEMMs in MXFP8, dothoosh.com MoK page, "Technical details of
-// the MoK mechanism").
+// MX grouped expert GEMMs: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 x E4M3 (MXFP8)
+// or E2M1 x E2M1 (MXFP4) operands, one E8M0 scale per 32 K-elements of every row of A
+// and B, fp32 accumulation (expert GEMMs in MXFP8, dothoosh.com MoK page, "Technical
+// details of the MoK mechanism"; MXFP4 as the narrower format of aikraft.ru MoK
+// article, section 03). The template parameter F picks the element format (MxFmt).
 //
 // Every operand is K-contiguous in HBM (the weights are pre-quantised in the
 // orientation each GEMM reads; the token-axis operands of the weight gradients are
@@ -17,6 +18,13 @@
 // is chunks 4ks..4ks+3, so lane half h reads chunks 4ks+h and 4ks+2+h (OpK::frag
 // positions 2ks and 2ks+1) and scale byte 2ks+h of the row's dword (shifted down by
 // 8h, opsel 2ks).
+//
+// E2M1 (pinned by an in-bounds probe against a CPU model with per-block scales): lane l
+// (half h) holds row l%32's k-block h (k 32h..32h+31) as 16 bytes, two codes per byte;
+// the scale of row i for k-block q again comes from lane i + 32q. A 128-byte tile row is
+// 256 elements (4 steps of 64); step ks is chunks 2ks and 2ks+1, lane half h reads chunk
+// 2ks+h (OpK::frag position ks), and its scale byte 2ks+h of the K-tile's 8 is byte
+// 2(ks%2)+h of scale dword ks/2 (shifted down by 8h, opsel 2(ks%2)).
 #include "gemm2.h"
 #include "kernels.h"
 #include "mx.h"
@@ -34,17 +42,17 @@ __device__ __forceinline__ void dma4_sv(const char* sbase, uint32_t voff, char* 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(l), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
-// Scale dwords of ROWS tile rows per K-tile. Wave w loads rows [w*RPW, (w+1)*RPW)
-// with lanes 0..RPW-1 (one DMA instruction per wave per stage, RPW >= 8 so the
-// instruction always has active lanes). K-tile kt's dwords sit kt * kstride bytes
-// after K-tile 0's: 4 for row-major scales; the matrix's rows * 4 for K-tile-major
-// ones, whose dwords for consecutive rows are contiguous (one 128-byte request per
-// 32 rows instead of one per row).
-template <int ROWS, int NF, int NW>
+// Scale dwords of ROWS tile rows per K-tile: SD per row (one per 128 elements of the
+// K-tile). Wave w loads rows [w*RPW, (w+1)*RPW) with lanes 0..RPW-1 (SD DMA
+// instructions per wave per stage, RPW >= 8 so each always has active lanes). The
+// dwords of 128-element slab j sit j * kstride bytes after slab 0's: 4 for row-major
+// scales; the matrix's rows * 4 for K-tile-major ones, whose dwords for consecutive
+// rows are contiguous (one 128-byte request per 32 rows instead of one per row).
+template <int ROWS, int NF, int NW, int SD = 1>
 struct OpScale {
   static constexpr int RPW = ROWS / NW;
   static_assert(ROWS % NW == 0 && RPW >= 8 && RPW <= 64, "scale rows per wave");
-  static constexpr int BYTES = ROWS * 4;
+  static constexpr int BYTES = SD * ROWS * 4;
   const char* sbase;
   uint32_t voff;
   uint32_t kstride;
@@ -63,11 +71,14 @@ struct OpScale {
     for (int f = 0; f < NF; ++f) foff[f] = 4u * (uint32_t)(frow(f) + (lane & 31));
   }
   __device__ __forceinline__ void issue(int kt, char* stage, int wave) const {
-    const char* b = uniform_ptr(sbase + (int64_t)kt * kstride);
-    if (active) dma4_sv(b, voff, stage + wave * RPW * 4);
+#pragma unroll
+    for (int d = 0; d < SD; ++d) {
+      const char* b = uniform_ptr(sbase + (int64_t)(SD * kt + d) * kstride);
+      if (active) dma4_sv(b, voff, stage + d * ROWS * 4 + wave * RPW * 4);
+    }
   }
-  __device__ __forceinline__ uint32_t get(const char* stage, int f, int lane) const {
-    return *reinterpret_cast<const uint32_t*>(stage + foff[f]) >> (8 * (lane >> 5));
+  __device__ __forceinline__ uint32_t get(const char* stage, int f, int lane, int d = 0) const {
+    return *reinterpret_cast<const uint32_t*>(stage + d * ROWS * 4 + foff[f]) >> (8 * (lane >> 5));
   }
 };
 
@@ -78,22 +89,29 @@ __device__ __forceinline__ v8i32_t join8(const uint4& lo, const uint4& hi) {
   return v;
 }
 
-// One 64-k step of the K-tile in `cur` (opsel = byte 2*KS of the shifted scale dwords).
-template <int KS, class Tl, class OA, class OB>
+// One 64-k step of the K-tile in `cur`. E4M3: 32 bytes per lane (frag positions 2KS,
+// 2KS+1), opsel = byte 2*KS of scale dword 0. E2M1: 16 bytes per lane (frag position KS;
+// the instruction reads the low 4 dwords), opsel = byte 2*(KS%2) of scale dword KS/2.
+template <int F, int KS, class Tl, class OA, class OB>
 __device__ __forceinline__ void mx_kstep(const OA& oa, const OB& ob, const char* ca, const char* cb,
-                                         const uint32_t (&xa)[Tl::FM], const uint32_t (&xb)[Tl::FN],
-                                         f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+                                         const uint32_t (&xa)[MxFmt<F>::SD][Tl::FM],
+                                         const uint32_t (&xb)[MxFmt<F>::SD][Tl::FN], f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+  constexpr int FMT = F == 0 ? 0 : 4;  // cbsz / blgp: E4M3 or E2M1
+  constexpr int D = F == 0 ? 0 : KS / 2, OP = F == 0 ? 2 * KS : 2 * (KS % 2);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
   v8i32_t a[Tl::FM], b[Tl::FN];
 #pragma unroll
-  for (int fm = 0; fm < Tl::FM; ++fm) a[fm] = join8(oa.frag(ca, fm, 2 * KS), oa.frag(ca, fm, 2 * KS + 1));
+  for (int fm = 0; fm < Tl::FM; ++fm)
+    a[fm] = F == 0 ? join8(oa.frag(ca, fm, 2 * KS), oa.frag(ca, fm, 2 * KS + 1)) : join8(oa.frag(ca, fm, KS), z);
 #pragma unroll
-  for (int fn = 0; fn < Tl::FN; ++fn) b[fn] = join8(ob.frag(cb, fn, 2 * KS), ob.frag(cb, fn, 2 * KS + 1));
+  for (int fn = 0; fn < Tl::FN; ++fn)
+    b[fn] = F == 0 ? join8(ob.frag(cb, fn, 2 * KS), ob.frag(cb, fn, 2 * KS + 1)) : join8(ob.frag(cb, fn, KS), z);
 #pragma unroll
   for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Tl::FN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fm], b[fn], acc[fm][fn], 0, 0, 2 * KS,
-                                                                    (int)xa[fm], 2 * KS, (int)xb[fn]);
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fm], b[fn], acc[fm][fn], FMT, FMT, OP,
+                                                                    (int)xa[D][fm], OP, (int)xb[D][fn]);
 }
 
 // STAGES-deep ring as in the bf16 core; a stage holds A rows, B rows, A scales, B scales.
@@ -118,13 +136,14 @@ __device__ __forceinline__ void mx_ring_prologue(const OA& oa, const OB& ob, con
   }
 }
 
-template <class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB>
+template <int F, class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB>
 __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
                                              char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
   static_assert(STAGES == 3, "the waits are written for 3 stages");
+  constexpr int SD = MxFmt<F>::SD;
   constexpr int OFF_B = OA::BYTES, OFF_SA = OA::BYTES + OB::BYTES, OFF_SB = OFF_SA + SA::BYTES;
   constexpr int STG = OFF_SB + SB::BYTES;
-  constexpr int NI = OA::NI + OB::NI + 2;
+  constexpr int NI = OA::NI + OB::NI + 2 * SD;
   zero_acc<Tl>(acc);
   for (int kt = 0; kt < KT; ++kt) {
     const bool pro = kt < STAGES - 1;  // issued by mx_ring_prologue, before any EXTRA stores
@@ -140,23 +159,33 @@ __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const S
       sb.issue(nk, st + OFF_SB, wave);
     }
     const char* cur = smem + (kt % STAGES) * STG;
-    uint32_t xa[Tl::FM], xb[Tl::FN];
+    uint32_t xa[SD][Tl::FM], xb[SD][Tl::FN];
 #pragma unroll
-    for (int fm = 0; fm < Tl::FM; ++fm) xa[fm] = sa.get(cur + OFF_SA, fm, lane);
+    for (int d = 0; d < SD; ++d) {
 #pragma unroll
-    for (int fn = 0; fn < Tl::FN; ++fn) xb[fn] = sb.get(cur + OFF_SB, fn, lane);
-    mx_kstep<0, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
-    if (nk < KT) ob.issue(nk, st + OFF_B, wave);
-    mx_kstep<1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      for (int fm = 0; fm < Tl::FM; ++fm) xa[d][fm] = sa.get(cur + OFF_SA, fm, lane, d);
+#pragma unroll
+      for (int fn = 0; fn < Tl::FN; ++fn) xb[d][fn] = sb.get(cur + OFF_SB, fn, lane, d);
+    }
+    mx_kstep<F, 0, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    if constexpr (F == 0) {
+      if (nk < KT) ob.issue(nk, st + OFF_B, wave);
+      mx_kstep<F, 1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    } else {
+      mx_kstep<F, 1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      if (nk < KT) ob.issue(nk, st + OFF_B, wave);
+      mx_kstep<F, 2, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      mx_kstep<F, 3, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    }
   }
   __syncthreads();
 }
 
-template <class Tl, int STAGES, class OA, class OB, class SA, class SB>
+template <int F, class Tl, int STAGES, class OA, class OB, class SA, class SB>
 __device__ __forceinline__ void main_loop_mx(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
                                              char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
   mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
-  mx_ring_loop<Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+  mx_ring_loop<F, Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
 }
 
 template <int BM, int BN>
@@ -181,12 +210,13 @@ struct MxRowArgs {
 
 enum MxKind { MFC1 = 0, MFC2 = 1, MDH = 2, MDX = 3 };
 
-template <int KIND, class Tl>
+template <int KIND, class Tl, int F>
 __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
+  using Fm = MxFmt<F>;
   using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
   using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
-  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
-  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW, Fm::SD>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW, Fm::SD>;
   constexpr int STG = OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES;
   __shared__ __align__(1024) char smem[kMxStages * STG];
   __shared__ int s_ts[kMaxEx + 1];
@@ -196,7 +226,8 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
   const int I2 = 2 * a.I;
   const int N = KIND == MFC1 ? I2 : (KIND == MFC2 || KIND == MDX ? a.H : a.I);
   const int K = KIND == MFC1 || KIND == MDH ? a.H : (KIND == MFC2 ? a.I : I2);
-  const int KB = K / 32;  // scale bytes per row
+  const int KB = K / 32;                       // scale bytes per row
+  const uint32_t KQ = (uint32_t)Fm::bytes(K);  // element bytes per row
   load_tile_start(a.sc, s_ts);
   for_each_row_tile(a.sc, s_ts, N / Tl::BN, blockIdx.x, gridDim.x, [&](const RowTile& t) {
     __syncthreads();
@@ -209,12 +240,11 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
     if constexpr (KIND == MFC1 || KIND == MDH) {
       // pull dispatch / reverse-combine: token rows gathered through perm (padding rows re-read row 0)
       const auto tok = [&](int row) { return (uint32_t)(s_slot[row < t.nrows ? row : 0] / a.k); };
-      oa.init(a.aq, [&](int row) -> uint32_t { return tok(row) * (uint32_t)K; }, frow_a, wave, lane);
+      oa.init(a.aq, [&](int row) -> uint32_t { return tok(row) * KQ; }, frow_a, wave, lane);
       sa.init(a.as, [&](int row) -> uint32_t { return tok(row) * 4u; }, frow_a, wave, lane, (uint32_t)a.T * 4u);
     } else {
       const auto rr = [&](int row) { return (uint32_t)(row < t.nrows ? row : 0); };
-      oa.init(a.aq + (int64_t)t.row0 * K, [&](int row) -> uint32_t { return rr(row) * (uint32_t)K; }, frow_a, wave,
-              lane);
+      oa.init(a.aq + (int64_t)t.row0 * KQ, [&](int row) -> uint32_t { return rr(row) * KQ; }, frow_a, wave, lane);
       sa.init(a.as + (int64_t)t.row0 * 4, [&](int row) -> uint32_t { return rr(row) * 4u; }, frow_a, wave, lane,
               (uint32_t)a.R * 4u);
     }
@@ -228,19 +258,18 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
         const int c = cbase + wj * (Tl::WTN / 2) + (fn >> 1) * 32 + (j & 31);
         return (uint32_t)((fn & 1) ? a.I + c : c);
       };
-      ob.init(a.wq + (int64_t)t.e * I2 * a.H, [&](int j) -> uint32_t { return wrow(j) * (uint32_t)K; }, frow_b, wave,
-              lane);
+      ob.init(a.wq + (int64_t)t.e * I2 * KQ, [&](int j) -> uint32_t { return wrow(j) * KQ; }, frow_b, wave, lane);
       sb.init(a.ws + (int64_t)t.e * I2 * KB, [&](int j) -> uint32_t { return wrow(j) * 4u; }, frow_b, wave, lane,
               (uint32_t)I2 * 4u);
     } else {
       // weight rows n*BN + j of expert e's [N][K] matrix
       const int64_t r0 = (int64_t)t.e * N + (int64_t)t.n * Tl::BN;
-      ob.init(a.wq + r0 * K, [&](int j) -> uint32_t { return (uint32_t)j * (uint32_t)K; }, frow_b, wave, lane);
+      ob.init(a.wq + r0 * KQ, [&](int j) -> uint32_t { return (uint32_t)j * KQ; }, frow_b, wave, lane);
       sb.init(a.ws + (int64_t)t.e * N * KB + (int64_t)t.n * Tl::BN * 4, [&](int j) -> uint32_t { return (uint32_t)j * 4u; },
               frow_b, wave, lane, (uint32_t)N * 4u);
     }
     f32x16_t acc[Tl::FM][Tl::FN];
-    main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, K / 128, smem, wave, lane, acc);
+    main_loop_mx<F, Tl, kMxStages>(oa, ob, sa, sb, K / Fm::KTILE, smem, wave, lane, acc);
 
     if constexpr (KIND == MFC1) {
       const int cbase = t.n * (Tl::BN / 2);
@@ -257,9 +286,7 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
         store16<bf16>(a.out0 + R * I2 + c, g);
         store16<bf16>(a.out0 + R * I2 + a.I + c, u);
         store16<bf16>(a.out1 + R * a.I + c, hv);
-        uint32_t sbyte;
-        const uint4 q = mx_quant16_pair(hv, &sbyte);
-        stg16(a.oq + R * a.I + c, q);
+        const uint32_t sbyte = Fm::quant_store16(hv, a.oq, R * a.I + c);
         if ((lane & 1) == 0) a.os[(int64_t)(c >> 7) * a.R * 4 + R * 4 + ((c >> 5) & 3)] = (uint8_t)sbyte;
       });
     } else if constexpr (KIND == MFC2 || KIND == MDX) {
@@ -291,11 +318,8 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
           round16_bf16(du);
           store16<bf16>(a.out0 + R * I2 + c, da);
           store16<bf16>(a.out0 + R * I2 + a.I + c, du);
-          uint32_t s1, s2;
-          const uint4 q1 = mx_quant16_pair(da, &s1);
-          const uint4 q2 = mx_quant16_pair(du, &s2);
-          stg16(a.oq + R * I2 + c, q1);
-          stg16(a.oq + R * I2 + a.I + c, q2);
+          const uint32_t s1 = Fm::quant_store16(da, a.oq, R * I2 + c);
+          const uint32_t s2 = Fm::quant_store16(du, a.oq, R * I2 + a.I + c);
           if ((lane & 1) == 0) {
             const int c2 = a.I + c;
             a.os[(int64_t)(c >> 7) * a.R * 4 + R * 4 + ((c >> 5) & 3)] = (uint8_t)s1;
@@ -314,8 +338,8 @@ __global__ __launch_bounds__(Tl::NT) void row_gemm_mx_kernel(MxRowArgs a) {
 }
 
 // Weight gradients: out[e] [M][N] = sum over k in e's padded segment of A[m][k] B[n][k],
-// A [M][kld] and B [N][kld] E4M3 with K-tile-major scales [kld/128][M][4], [kld/128][N][4]; e's segment is
-// columns pofs[e] .. pofs[e+1] (a multiple of 128; empty -> zeros written).
+// A [M][kld] and B [N][kld] elements with K-tile-major scales [kld/128][M][4], [kld/128][N][4]; e's segment is
+// columns pofs[e] .. pofs[e+1] (a multiple of the K-tile; empty -> zeros written).
 struct MxDwArgs {
   const int32_t* pofs;
   const uint8_t *aq, *as, *bq, *bs;
@@ -325,12 +349,13 @@ struct MxDwArgs {
   Guard guard;
 };
 
-template <class Tl, typename TO>
+template <class Tl, typename TO, int F>
 __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
+  using Fm = MxFmt<F>;
   using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
   using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
-  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
-  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW, Fm::SD>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW, Fm::SD>;
   __shared__ __align__(1024) char smem[kMxStages * (OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES)];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
@@ -341,23 +366,24 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
   const int rem = L - e * MT * NT;
   const int mt = rem / NT, nt = rem - mt * NT;
   const int64_t k0 = a.pofs[e];
-  const int KT = (int)((a.pofs[e + 1] - k0) / 128);
+  const int KT = (int)((a.pofs[e + 1] - k0) / Fm::KTILE);
+  const int64_t ldq = Fm::bytes(a.kld), k0q = Fm::bytes(k0);
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
   const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
   OA oa;
   SA sa;
   OB ob;
   SB sb;
-  oa.init(a.aq + (int64_t)mt * Tl::BM * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+  oa.init(a.aq + (int64_t)mt * Tl::BM * ldq + k0q, [&](int r) -> uint32_t { return (uint32_t)(r * ldq); },
           frow_a, wave, lane);
   sa.init(a.as + (k0 / 128) * a.M * 4 + (int64_t)mt * Tl::BM * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
           frow_a, wave, lane, (uint32_t)a.M * 4u);
-  ob.init(a.bq + (int64_t)nt * Tl::BN * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+  ob.init(a.bq + (int64_t)nt * Tl::BN * ldq + k0q, [&](int r) -> uint32_t { return (uint32_t)(r * ldq); },
           frow_b, wave, lane);
   sb.init(a.bs + (k0 / 128) * a.N * 4 + (int64_t)nt * Tl::BN * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
           frow_b, wave, lane, (uint32_t)a.N * 4u);
   f32x16_t acc[Tl::FM][Tl::FN];
-  main_loop_mx<Tl, kMxStages>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+  main_loop_mx<F, Tl, kMxStages>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
   TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
   epilogue16<Tl, false>(acc, smem, wave, wm, wn, lane, [&](int row, int col, const float (&g)[16], const float (&)[16]) {
     store16<TO>(out + (int64_t)row * a.N + col, g);
@@ -369,12 +395,13 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
 // of the (expert, M-tile, N-tile) range; the next tile's first K-tiles are issued
 // before this tile's epilogue, whose stores then drain under the next K-loop. The
 // epilogue's per-wave patches use the ring stage that this prologue leaves free.
-template <class Tl>
+template <class Tl, int F>
 __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
+  using Fm = MxFmt<F>;
   using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
   using OB = OpK<Tl::BN, Tl::FN, Tl::NW>;
-  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW>;
-  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW>;
+  using SA = OpScale<Tl::BM, Tl::FM, Tl::NW, Fm::SD>;
+  using SB = OpScale<Tl::BN, Tl::FN, Tl::NW, Fm::SD>;
   constexpr int STAGES = kMxStages;
   constexpr int STG = OA::BYTES + OB::BYTES + SA::BYTES + SB::BYTES;
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
@@ -391,8 +418,8 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   const int li = blockIdx.x / P;
   if (guard_fail(a.guard)) return;
   int64_t lo, hi;
-  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.pofs[e + 1] - a.pofs[e]) / 128; }, s_u, P, xcd, lo,
-                   hi);
+  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.pofs[e + 1] - a.pofs[e]) / Fm::KTILE; }, s_u, P,
+                   xcd, lo, hi);
   int64_t L = lo + li;
   if (L >= hi) return;
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
@@ -402,18 +429,19 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   SA sa;
   SB sb;
   int e = 0, mt = 0, nt = 0, KT = 0;
+  const int64_t ldq = Fm::bytes(a.kld);
   const auto setup = [&](int64_t l) {
     e = __builtin_amdgcn_readfirstlane((int)(l / (MT * NT)));
     const int rem = (int)(l - (int64_t)e * MT * NT);
     mt = __builtin_amdgcn_readfirstlane(rem / NT);
     nt = __builtin_amdgcn_readfirstlane(rem - mt * NT);
     const int64_t k0 = __builtin_amdgcn_readfirstlane(a.pofs[e]);
-    KT = __builtin_amdgcn_readfirstlane((int)((a.pofs[e + 1] - k0) / 128));
-    oa.init(a.aq + (int64_t)mt * Tl::BM * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+    KT = __builtin_amdgcn_readfirstlane((int)((a.pofs[e + 1] - k0) / Fm::KTILE));
+    oa.init(a.aq + (int64_t)mt * Tl::BM * ldq + Fm::bytes(k0), [&](int r) -> uint32_t { return (uint32_t)(r * ldq); },
             frow_a, wave, lane);
     sa.init(a.as + (k0 / 128) * a.M * 4 + (int64_t)mt * Tl::BM * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
             frow_a, wave, lane, (uint32_t)a.M * 4u);
-    ob.init(a.bq + (int64_t)nt * Tl::BN * a.kld + k0, [&](int r) -> uint32_t { return (uint32_t)(r * a.kld); },
+    ob.init(a.bq + (int64_t)nt * Tl::BN * ldq + Fm::bytes(k0), [&](int r) -> uint32_t { return (uint32_t)(r * ldq); },
             frow_b, wave, lane);
     sb.init(a.bs + (k0 / 128) * a.N * 4 + (int64_t)nt * Tl::BN * 4, [&](int r) -> uint32_t { return (uint32_t)r * 4u; },
             frow_b, wave, lane, (uint32_t)a.N * 4u);
@@ -424,9 +452,9 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   for (;;) {
     f32x16_t acc[Tl::FM][Tl::FN];
     if (first)
-      mx_ring_loop<Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+      mx_ring_loop<F, Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
     else
-      mx_ring_loop<Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+      mx_ring_loop<F, Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
     bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
     const int64_t Ln = L + nx;
     if (Ln < hi) {
@@ -450,7 +478,10 @@ static hipError_t row_launch_mx(const Ctx& c, const MxRowArgs& a, int N) {
   int g = c.grid > 0 ? c.grid : c.num_cu;
   const int64_t upper = (int64_t)c.max_tiles * (N / BN);
   if (g > upper) g = (int)std::max<int64_t>(upper, 1);
-  hipLaunchKernelGGL((row_gemm_mx_kernel<KIND, Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a);
+  if (c.mx4)
+    hipLaunchKernelGGL((row_gemm_mx_kernel<KIND, Tl, 1>), dim3(g), dim3(Tl::NT), 0, c.s, a);
+  else
+    hipLaunchKernelGGL((row_gemm_mx_kernel<KIND, Tl, 0>), dim3(g), dim3(Tl::NT), 0, c.s, a);
   return hipGetLastError();
 }
 
@@ -534,10 +565,16 @@ static hipError_t dw_launch_mx(const Ctx& c, const MxDwArgs& a) {
   if (blocks == 0) return hipSuccess;
   if (!c.wgrad_f32) {
     const int g = (int)std::min<int64_t>(c.grid > 0 ? c.grid : c.num_cu, blocks);
-    hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    if (c.mx4)
+      hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 1>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    else
+      hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 0>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((dw_mx_kernel<Tl, float>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
+  if (c.mx4)
+    hipLaunchKernelGGL((dw_mx_kernel<Tl, float, 1>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
+  else
+    hipLaunchKernelGGL((dw_mx_kernel<Tl, float, 0>), dim3((unsigned)blocks), dim3(Tl::NT), 0, c.s, a);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct Ctx {
   int num_cu;
   int grid;        // persistent GEMM grid
   int gemm;        // expert-GEMM dtype (mok_dtype)
+  bool mx4;        // MX GEMMs with E2M1 elements (MOK_MXFP4)
   hipStream_t s;
   Guard guard;     // schedule header check (every kernel of forward/backward)
   // schedule table (device)

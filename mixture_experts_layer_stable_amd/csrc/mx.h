@@ -1,5 +1,5 @@
-// MXFP8 (OCP Microscaling v1.0) on gfx950: FP8 E4M3 elements with one E8M0
-// scale per 32 values.
+// MX formats (OCP Microscaling v1.0) on gfx950: MXFP8 (FP8 E4M3 elements) and MXFP4
+// (FP4 E2M1 elements), one E8M0 scale per 32 values.
 //
 // Block quantisation (the block's values are finite and already rounded to bf16):
 //   amax = largest magnitude; s = floor(log2 amax) - 8 (8 = exponent of E4M3's
@@ -49,6 +49,69 @@ __device__ __forceinline__ uint4 mx_quant16_pair(const float (&v)[16], uint32_t*
   *sbyte = b;
   return mx_pack16(v, mx_inv_scale(b));
 }
+
+// MXFP4 (OCP MX v1.0 FP4 E2M1 elements, same E8M0 block scale): s = floor(log2 amax) - 2
+// (2 = exponent of E2M1's largest normal, 6 = 1.5 * 2^2), so the scale byte is
+// max(exponent field of amax - 2, 0); elements are v * 2^-s rounded to nearest even
+// onto {0, 0.5, 1, 1.5, 2, 3, 4, 6} and saturated at 6. Codes: sign bit 3, exponent
+// bits 2..1, mantissa bit 0 (the magnitude's code is its index in that list), two per
+// byte, the even element in the low nibble. The MFMA takes a row's 32-element block as
+// 16 consecutive bytes in one lane.
+__device__ __forceinline__ uint32_t mx4_scale_byte(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return (uint32_t)max(e - 2, 0);
+}
+
+// Nearest E2M1 code of v (|v| < 8 after scaling; larger saturates): the magnitude code
+// counts the midpoints below |v|, a midpoint itself going to the code with mantissa 0.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | (v < 0.0f ? 8u : 0u);
+}
+
+// 16 values -> 8 bytes of E2M1 codes of v * inv.
+__device__ __forceinline__ uint2 mx4_pack16(const float (&v)[16], float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_code(v[i] * inv) << (4 * (i & 7));
+  return make_uint2(w[0], w[1]);
+}
+
+// As mx_quant16_pair, for E2M1: this lane's 8 bytes of the pair's 32-element block.
+__device__ __forceinline__ uint2 mx4_quant16_pair(const float (&v)[16], uint32_t* sbyte) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  const uint32_t b = mx4_scale_byte(m);
+  *sbyte = b;
+  return mx4_pack16(v, mx_inv_scale(b));
+}
+
+// Element format of an MX GEMM path: 0 = E4M3 (MXFP8), 1 = E2M1 (MXFP4).
+// KTILE: elements per 128-byte tile row (one K-tile); SD: scale dwords per row and
+// K-tile (the scale arrays keep 4 bytes per 128 elements in either format).
+template <int F>
+struct MxFmt {
+  static constexpr int BITS = F == 0 ? 8 : 4;
+  static constexpr int KTILE = F == 0 ? 128 : 256;
+  static constexpr int SD = KTILE / 128;
+  static __device__ __forceinline__ int64_t bytes(int64_t elems) { return F == 0 ? elems : elems / 2; }
+  // quantise a lane pair's 32-element block (16 values here) and store this lane's part
+  // of it at element offset `elem` of q (elem a multiple of 16)
+  static __device__ __forceinline__ uint32_t quant_store16(const float (&v)[16], uint8_t* q, int64_t elem) {
+    uint32_t sb;
+    if constexpr (F == 0) {
+      stg16(q + elem, mx_quant16_pair(v, &sb));
+    } else {
+      const uint2 o = mx4_quant16_pair(v, &sb);
+      *reinterpret_cast<uint2*>(q + elem / 2) = o;
+    }
+    return sb;
+  }
+};
 
 // Round 16 floats to bf16 values (as floats): the stored value a quantiser sees.
 __device__ __forceinline__ void round16_bf16(float (&v)[16]) {

@@ -1,4 +1,5 @@
-// MXFP8 quantisers and the deferred weight-gradient bookkeeping (HBM-bound kernels).
+// MX quantisers (MXFP8 and MXFP4 elements, template parameter F of MxFmt) and the
+// deferred weight-gradient bookkeeping (HBM-bound kernels).
 //
 //  quant_rows   blocks of 32 along each row: x and dY rows (K = H of fc1 / dh) and the
 //               forward weight orientations W1 (rows along H) and W2 (rows along I).
@@ -7,8 +8,9 @@
 //               operands of the weight-gradient GEMMs (dO, h, dGU, x over each
 //               expert's routed rows of the whole step).
 //  flush_table  per expert: rows over all stashed micro-batches, and the K offset of its
-//               segment in the token-axis operands (segments padded to 128 rows with
-//               zero rows, i.e. all-zero blocks, which add nothing).
+//               segment in the token-axis operands (segments padded to a whole K-tile,
+//               128 rows for MXFP8 and 256 for MXFP4, with zero rows, i.e. all-zero
+//               blocks, which add nothing).
 //  rowmap       padded segment row -> stash row (micro-batch m's routed row r is stash
 //               row m*R + r); -1 for padding.
 //  dwr_stash    dWr[e] = sum over e's rows of the step (micro-batch then slot order) of
@@ -27,6 +29,7 @@ static unsigned nblk(int64_t n, int b = 256) { return (unsigned)((n + b - 1) / b
 // Scale byte of block b (32 features) of row r: row-major (kmaj_rows = 0) at
 // r * F/32 + b; K-tile-major (kmaj_rows > 0 = rows per matrix) at
 // [z][b/4][r % kmaj_rows][b % 4] with z = r / kmaj_rows.
+template <int FM>
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(Guard gd, const bf16* __restrict__ src, int64_t nvec,
                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s, int F,
                                                             int64_t kmaj_rows) {
@@ -34,9 +37,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(Guard gd, const bf16
   if (guard_fail(gd) || v >= nvec) return;  // nvec and blockDim are even: a pair leaves together
   float f[16];
   load16<bf16>(src + v * 16, f);
-  uint32_t sb;
-  const uint4 o = mx_quant16_pair(f, &sb);
-  stg16(q + v * 16, o);
+  const uint32_t sb = MxFmt<FM>::quant_store16(f, q, v * 16);
   if ((v & 1) == 0) {
     int64_t i = v >> 1;
     if (kmaj_rows > 0) {
@@ -51,15 +52,20 @@ hipError_t launch_mx_quant_rows(const Ctx& c, const void* src, int64_t rows, int
                                 int64_t kmaj_rows) {
   const int64_t nvec = rows * (F / 16);
   if (nvec == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(nblk(nvec)), dim3(256), 0, c.s, c.guard, (const bf16*)src, nvec, (uint8_t*)q,
-                     (uint8_t*)s, F, kmaj_rows);
+  if (c.mx4)
+    hipLaunchKernelGGL(mx_quant_rows_kernel<1>, dim3(nblk(nvec)), dim3(256), 0, c.s, c.guard, (const bf16*)src, nvec,
+                       (uint8_t*)q, (uint8_t*)s, F, kmaj_rows);
+  else
+    hipLaunchKernelGGL(mx_quant_rows_kernel<0>, dim3(nblk(nvec)), dim3(256), 0, c.s, c.guard, (const bf16*)src, nvec,
+                       (uint8_t*)q, (uint8_t*)s, F, kmaj_rows);
   return hipGetLastError();
 }
 
 // Transposing quantiser. Matrix z = blockIdx.z; logical row r in [0, K) reads
 // physical row rowmap[r] (rowmap != nullptr; < 0 = zero row) or r of
 // src + z * src_mat, ld elements per physical row; feature f in [0, F).
-// Writes q[(z*F + f) * out_ld + r] and the scale of block b = r/32 K-tile-major,
+// Writes element q[(z*F + f) * out_ld + r] (out_ld in elements) and the scale of block
+// b = r/32 K-tile-major,
 // s[z*F*(out_ld/32) + (b/4)*F*4 + f*4 + b%4]: each 128-row K-tile's scale dwords of
 // consecutive features are contiguous.
 // Workgroup: 128 logical rows x 64 features. Wave w quantises features 16w .. 16w+15;
@@ -81,6 +87,7 @@ struct ColQuantArgs {
   Guard guard;
 };
 
+template <int FM>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
   __shared__ float tile[128][65];
   const int r0 = blockIdx.x * 128, f0 = blockIdx.y * 64, z = blockIdx.z;
@@ -109,18 +116,28 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][pf]));
-  const uint32_t sb = mx_scale_byte(m);
-  const float inv = mx_inv_scale(sb);
-  uint32_t w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = 32 * b + 4 * j;
-    w[j] = mx_pack4(tile[i][pf], tile[i + 1][pf], tile[i + 2][pf], tile[i + 3][pf], inv);
-  }
   const int64_t orow = (int64_t)z * a.F + f0 + f;
-  uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;
-  stg16(qo, make_uint4(w[0], w[1], w[2], w[3]));
-  stg16(qo + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  uint32_t sb;
+  if constexpr (FM == 0) {
+    sb = mx_scale_byte(m);
+    const float inv = mx_inv_scale(sb);
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = 32 * b + 4 * j;
+      w[j] = mx_pack4(tile[i][pf], tile[i + 1][pf], tile[i + 2][pf], tile[i + 3][pf], inv);
+    }
+    uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;
+    stg16(qo, make_uint4(w[0], w[1], w[2], w[3]));
+    stg16(qo + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  } else {
+    sb = mx4_scale_byte(m);
+    const float inv = mx_inv_scale(sb);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_code(tile[32 * b + i][pf] * inv) << (4 * (i & 7));
+    stg16(a.q + orow * (a.out_ld / 2) + (r0 + 32 * b) / 2, make_uint4(w[0], w[1], w[2], w[3]));
+  }
   const int64_t kb = r0 / 32 + b;
   a.s[(int64_t)z * a.F * (a.out_ld / 32) + (kb >> 2) * a.F * 4 + (int64_t)(f0 + f) * 4 + (kb & 3)] = (uint8_t)sb;
 }
@@ -129,13 +146,16 @@ hipError_t launch_mx_quant_cols(const Ctx& c, const void* src, int64_t src_mat, 
                                 const int32_t* kdev, int K, int F, int mats, int64_t out_ld, void* q, void* s) {
   if (K == 0 || F == 0 || mats == 0) return hipSuccess;
   ColQuantArgs a{(const bf16*)src, src_mat, ld, rowmap, kdev, F, out_ld, (uint8_t*)q, (uint8_t*)s, c.guard};
-  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3(K / 128, F / 64, mats), dim3(256), 0, c.s, a);
+  if (c.mx4)
+    hipLaunchKernelGGL(mx_quant_cols_kernel<1>, dim3(K / 128, F / 64, mats), dim3(256), 0, c.s, a);
+  else
+    hipLaunchKernelGGL(mx_quant_cols_kernel<0>, dim3(K / 128, F / 64, mats), dim3(256), 0, c.s, a);
   return hipGetLastError();
 }
 
 // One workgroup of 1024 threads (E <= 1024). counts is [M][E].
 __global__ __launch_bounds__(1024) void mx_flush_table_kernel(Guard gd, const int32_t* __restrict__ counts, int M,
-                                                              int E, int32_t* __restrict__ gcnt,
+                                                              int E, int kt, int32_t* __restrict__ gcnt,
                                                               int32_t* __restrict__ pofs) {
   __shared__ int sc[1024];
   if (guard_fail(gd)) return;
@@ -143,7 +163,7 @@ __global__ __launch_bounds__(1024) void mx_flush_table_kernel(Guard gd, const in
   int c = 0;
   if (e < E)
     for (int m = 0; m < M; ++m) c += counts[(int64_t)m * E + e];
-  const int p = (c + 127) & ~127;
+  const int p = (c + kt - 1) / kt * kt;
   sc[e] = p;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
@@ -190,7 +210,8 @@ __global__ __launch_bounds__(256) void mx_rowmap_kernel(Guard gd, const int32_t*
 
 hipError_t launch_mx_flush_table(const Ctx& c, const int32_t* counts, const int32_t* offsets, int M, int32_t* gcnt,
                                  int32_t* pofs, int64_t kmax, int32_t* rowmap) {
-  hipLaunchKernelGGL(mx_flush_table_kernel, dim3(1), dim3(1024), 0, c.s, c.guard, counts, M, c.E, gcnt, pofs);
+  hipLaunchKernelGGL(mx_flush_table_kernel, dim3(1), dim3(1024), 0, c.s, c.guard, counts, M, c.E, c.mx4 ? 256 : 128,
+                     gcnt, pofs);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(mx_rowmap_kernel, dim3(nblk(kmax)), dim3(256), 0, c.s, c.guard, counts, offsets, M, c.E, c.R, gcnt, pofs,
                      kmax, rowmap);

@@ -86,7 +86,7 @@ class Workload:
     k: int
     I: int
     act: str            # activation / weight storage dtype: 'f32' or 'bf16'
-    gemm: str           # expert-GEMM operand format: 'f32', 'bf16' or 'mxfp8'
+    gemm: str           # expert-GEMM operand format: 'f32', 'bf16', 'mxfp8' or 'mxfp4'
     backward: bool
     zipf: bool          # imbalanced routing via the Zipf-ranked router bias
     micro_batches: int = 1

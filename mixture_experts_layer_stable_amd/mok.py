@@ -17,12 +17,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmok.so")
 
-F32, BF16, MXFP8 = 0, 1, 2
+F32, BF16, MXFP8, MXFP4 = 0, 1, 2, 3
 FLAG_WGRAD_F32 = 1
 FLAG_WGRAD_DEFER = 2
 FLAG_REPLAY = 4
 FLAG_FUSED = 8
-DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8}
+DTYPES = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8, "mxfp4": MXFP4}
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
 STATUS = {0: "MOK_OK", 1: "MOK_ERR_NULL", 2: "MOK_ERR_ALIGN", 3: "MOK_ERR_SHAPE", 4: "MOK_ERR_DTYPE",
@@ -147,7 +147,7 @@ class Desc:
 
     @property
     def mx(self) -> bool:
-        return self.gemm == MXFP8
+        return self.gemm in (MXFP8, MXFP4)
 
     @property
     def R(self) -> int:
@@ -244,16 +244,18 @@ def check_schedule(d: Desc, sched, where="schedule"):
 
 
 class MxWeights:
-    """Device tensors of the MXFP8 weight orientations (mok_mx_weights), filled by weights_quantize."""
+    """Device tensors of the MX weight orientations (mok_mx_weights), filled by weights_quantize.
+    Element bytes [E][rows][K] (MXFP8) or [E][rows][K/2] (MXFP4, two E2M1 codes per byte)."""
 
     def __init__(self, d: Desc, device="cuda"):
         E, H, I = d.E, d.H, d.I
         u8 = dict(dtype=torch.uint8, device=device)
+        q = (lambda k: k // 2) if d.gemm == MXFP4 else (lambda k: k)
         # scales K-tile-major: [E][K/128][rows][4]
-        self.w1q, self.w1s = torch.empty(E, 2 * I, H, **u8), torch.empty(E, H // 128, 2 * I, 4, **u8)
-        self.w2q, self.w2s = torch.empty(E, H, I, **u8), torch.empty(E, I // 128, H, 4, **u8)
-        self.w2tq, self.w2ts = torch.empty(E, I, H, **u8), torch.empty(E, H // 128, I, 4, **u8)
-        self.w1tq, self.w1ts = torch.empty(E, H, 2 * I, **u8), torch.empty(E, 2 * I // 128, H, 4, **u8)
+        self.w1q, self.w1s = torch.empty(E, 2 * I, q(H), **u8), torch.empty(E, H // 128, 2 * I, 4, **u8)
+        self.w2q, self.w2s = torch.empty(E, H, q(I), **u8), torch.empty(E, I // 128, H, 4, **u8)
+        self.w2tq, self.w2ts = torch.empty(E, I, q(H), **u8), torch.empty(E, H // 128, I, 4, **u8)
+        self.w1tq, self.w1ts = torch.empty(E, H, q(2 * I), **u8), torch.empty(E, 2 * I // 128, H, 4, **u8)
 
     def c(self) -> _MxWeights:
         return _MxWeights(*[getattr(self, n).data_ptr() for n in MX_FIELDS])

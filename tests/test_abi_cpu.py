@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(mok):
     for n in _declared():
         assert hasattr(lib, n), n
     assert set(_declared()) == set(mok.EXPORTS)
-    assert mok.version() == 300
+    assert mok.version() == 301
 
 
 def test_status_strings(mok):
@@ -58,6 +58,8 @@ def _d(mok, **kw):
     (dict(flags=2), 4), (dict(mb_count=2), 3), (dict(gemm=2, mb_count=2, mb_index=2), 3),
     (dict(gemm=2, mb_index=-1), 3), (dict(gemm=2, mb_count=-1), 3), (dict(gemm=2, ring=-1), 3),
     (dict(gemm=2, T=1 << 20, H=4096, E=8, k=8, mb_count=64), 3),
+    (dict(gemm=3, H=128), 3), (dict(gemm=3, H=256, I=128), 3), (dict(act=0, gemm=3, H=256), 4),
+    (dict(gemm=4), 4),
 ])
 def test_descriptor_validation(mok, kw, status):
     with pytest.raises(mok.MokError) as ei:
@@ -90,6 +92,23 @@ def test_mxfp8_workspace_sizes(mok):
         flush = kmax * (2 * d.H + d.I + 2 * d.I) * 33 // 32 + 4 * kmax
         assert s["bwd_ws"] >= S * (d.T * d.H + R * 2 * d.I + 2 * R * d.H) + stash + flush
         assert s["saved"] == mok.workspace_query(_d(mok, T=256, H=256, E=8, k=2, I=128))["saved"]
+
+
+def test_mxfp4_workspace_sizes(mok):
+    """MXFP4: quantised rows hold two E2M1 codes per byte (scales as for MXFP8), and the
+    token-axis operands are padded to 256 rows per expert."""
+    for M, S in ((1, 1), (8, 2)):
+        d4 = _d(mok, T=256, H=256, E=8, k=2, I=256, gemm=mok.MXFP4, mb_count=M, ring=S)
+        d8 = _d(mok, T=256, H=256, E=8, k=2, I=256, gemm=mok.MXFP8, mb_count=M, ring=S)
+        s4, s8 = mok.workspace_query(d4), mok.workspace_query(d8)
+        R = d4.R
+        assert s4["fwd_ws"] >= S * (d4.T * d4.H * 17 // 32 + R * d4.I * 17 // 32 + 2 * R * d4.H)
+        assert s4["fwd_ws"] < s8["fwd_ws"]
+        kmax = M * R + 256 * d4.E
+        flush = kmax * (2 * d4.H + d4.I + 2 * d4.I) * 17 // 32 + 4 * kmax
+        stash = M * R * (2 * d4.H + 2 * d4.H + 2 * d4.I + 4 * d4.I + 8)
+        assert s4["bwd_ws"] >= S * (d4.T * d4.H // 2 + R * d4.I + 2 * R * d4.H) + stash + flush
+        assert s4["saved"] == s8["saved"]
 
 
 def test_null_and_alignment_rejected_before_launch(mok):

@@ -83,9 +83,9 @@ def _case(w):
     return x, dy, wr, b, w1, w2
 
 
-def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True, wgrad_f32=False):
+def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True, wgrad_f32=False, gemm=None):
     mok = _mok()
-    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m,
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8 if gemm is None else gemm, tile_m=tile_m,
                  flags=mok.FLAG_WGRAD_F32 if wgrad_f32 else 0)
     buf = mok.Buffers(d, DEV, wgrad_f32=wgrad_f32)
     q = mok.MxWeights(d, DEV)
@@ -105,10 +105,10 @@ def _run_whole(w, x, dy, wr, b, w1, w2, tile_m=0, router_grad=True, wgrad_f32=Fa
     return out
 
 
-def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0, flags=0):
+def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0, flags=0, gemm=None):
     mok = _mok()
-    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, tile_m=tile_m, mb_count=M, ring=ring,
-                 grid=grid, flags=flags)
+    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8 if gemm is None else gemm,
+                 tile_m=tile_m, mb_count=M, ring=ring, grid=grid, flags=flags)
     st = mok.StreamedStep(d, DEV)
     q = mok.MxWeights(d, DEV)
     mok.weights_quantize(d, w1.to(DEV), w2.to(DEV), q)
@@ -118,12 +118,12 @@ def _run_streamed(w, M, ring, x, dy, wr, b, w1, w2, tile_m=0, grid=0, flags=0):
                 dw1=st.dw1.cpu(), dw2=st.dw2.cpu(), dwr=st.dwr.cpu())
 
 
-def _oracle(w, x, dy, wr, b, w1, w2, wfmt="bf16"):
+def _oracle(w, x, dy, wr, b, w1, w2, wfmt="bf16", fmt="e4m3"):
     xs, dys, wrs = x.float().numpy(), dy.float().numpy(), wr.float().numpy()
     z, idx, g = orc.route(xs, wrs, w.k, None if b is None else b.numpy())
     W = orc.DenseWeights(w1.float().numpy(), w2.float().numpy())
-    f = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I)
-    bw = orc.mx.backward_mx(xs, W, wrs, idx, g, f, dys, w.I, wfmt=wfmt)
+    f = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, fmt=fmt)
+    bw = orc.mx.backward_mx(xs, W, wrs, idx, g, f, dys, w.I, wfmt=wfmt, fmt=fmt)
     return idx, g, f, bw
 
 
@@ -302,14 +302,14 @@ def _bf16_rows(buf: torch.Tensor, off: int, rows: int, cols: int) -> np.ndarray:
     return buf[off: off + 2 * rows * cols].cpu().view(torch.bfloat16).view(rows, cols).double().numpy()
 
 
-def _compare_blocks(name, got_el, got_s, ref_vals, gate_vals, axis_rows=False):
+def _compare_blocks(name, got_el, got_s, ref_vals, gate_vals, axis_rows=False, fmt="e4m3"):
     """got_el/got_s: decoded GPU elements and scale exponents; ref_vals: the oracle's bf16
     values (blocks of 32 along the last axis, or along axis 0 when axis_rows); gate_vals:
     the GPU's stored bf16 values of the same elements."""
     if axis_rows:
         got_el, ref_vals, gate_vals = got_el.T, ref_vals.T, gate_vals.T
         got_s = got_s.T
-    el, s = orc.mx.mx_quantize(ref_vals, -1)
+    el, s = orc.mx.mx_quantize(ref_vals, -1, fmt)
     nb = ref_vals.shape[-1] // 32
     same = np.all((ref_vals == gate_vals).reshape(ref_vals.shape[:-1] + (nb, 32)), axis=-1)
     frac = same.mean()
