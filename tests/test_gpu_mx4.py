@@ -233,3 +233,38 @@ def test_mx4_step_quantisers_bit_exact():
                                    ref, gate_v, axis_rows=True, fmt="e2m1")
         fracs[name] = tot
     print("blocks compared:", {k_: "%.3f" % v for k_, v in fracs.items()}, flush=True)
+
+
+def test_mx4_wgrad_f32():
+    """MXFP4 with MOK_FLAG_WGRAD_F32: fp32 weight gradients (one output tile per workgroup)
+    and fp32 dWr, against the oracle's MXFP4 step with dW kept in fp32."""
+    mok = _mok()
+    w = inputs.replace(MX4_CASES["imbalanced"], T=512, H=256, E=8, k=2, I=256)
+    x, dy, wr, b, w1, w2 = _case(w)
+    g = _run_whole(w, x, dy, wr, b, w1, w2, wgrad_f32=True, gemm=mok.MXFP4)
+    assert g["dw1"].dtype == torch.float32 and g["dwr"].dtype == torch.float32
+    idx, gate, f, bw = _oracle(w, x, dy, wr, b, w1, w2, wfmt="f32", fmt="e2m1")
+    np.testing.assert_array_equal(g["idx"], idx)
+    errs = {"dw1": rel_fro(np64(g["dw1"]), np.stack([bw["dw1"][e] for e in range(w.E)])),
+            "dw2": rel_fro(np64(g["dw2"]), np.stack([bw["dw2"][e] for e in range(w.E)])),
+            "dwr": rel_fro(np64(g["dwr"]), bw["dwr"]), "dx": rel_fro(np64(g["dx"]), bw["dx"])}
+    print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_MX4, (k, v)
+
+
+def test_mx4_grids_and_replay_bit_identical():
+    """Persistent grids of 1, 7 and 300 workgroups, and forward-activation replay, give the
+    streamed MXFP4 step's bits (4 micro-batches, 2-slot ring)."""
+    mok = _mok()
+    w = inputs.replace(MX4_CASES["imbalanced"], T=1024)
+    case = _case(w)
+    ref = _run_streamed(w, 4, 2, *case, gemm=mok.MXFP4)
+    runs = [("grid %d" % g, dict(grid=g)) for g in (1, 7, 300)] + [("replay", dict(flags=mok.FLAG_REPLAY))]
+    for label, kw in runs:
+        print("case MXFP4 streamed 4x,", label, flush=True)
+        got = _run_streamed(w, 4, 2, *case, gemm=mok.MXFP4, **kw)
+        for n in ref:
+            a, c = got[n], ref[n]
+            same = np.array_equal(a, c) if isinstance(a, np.ndarray) else torch.equal(a, c)
+            assert same, (label, n)
