@@ -103,7 +103,8 @@ def oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt="bf16", mx=False, wo
     then the token side: the slot-order combine and the router backward / dX reduction
     (oracle.combine, oracle.reduce_backward). Bit for bit the oracle's whole-step result,
     which a CPU test checks; the full-size GPU tests use it to keep the oracle's passes over
-    hundreds of experts within minutes."""
+    hundreds of experts within minutes. mx: False, or the MX element format ('e4m3', 'e2m1';
+    True means 'e4m3')."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
@@ -119,9 +120,11 @@ def _oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt, mx, workers, Threa
     def rows_of(ch):
         return np.nonzero(np.isin(flat, ch))[0]
 
+    mxf = "e4m3" if mx is True else mx
+
     def fwd(ch):
         if mx:
-            return ch, orc.mx.forward_mx(x, W, idx, gate, E, I, experts=ch)
+            return ch, orc.mx.forward_mx(x, W, idx, gate, E, I, experts=ch, fmt=mxf)
         return ch, orc.forward(x, W, idx, gate, fmt, E, I, experts=ch)
 
     with ThreadPoolExecutor(len(chunks)) as ex:
@@ -135,7 +138,7 @@ def _oracle_step_parallel(x, W, wr, idx, gate, dy, E, I, fmt, mx, workers, Threa
 
     def bwd(ch):
         if mx:
-            return ch, orc.mx.backward_mx(x, W, wr, idx, gate, f, dy, I, experts=ch)
+            return ch, orc.mx.backward_mx(x, W, wr, idx, gate, f, dy, I, experts=ch, fmt=mxf)
         return ch, orc.backward(x, W, wr, idx, gate, f, dy, fmt, I, experts=ch)
 
     with ThreadPoolExecutor(len(chunks)) as ex:

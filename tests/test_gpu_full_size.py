@@ -159,8 +159,10 @@ def test_kimi_k2_full_size_zipf_imbalanced():
     _run(inputs.replace(inputs.WORKLOADS["kimi_k2_mxfp8_stream"], gemm="bf16", micro_batches=1))
 
 
-def test_kimi_k2_mxfp8_streamed_full_size():
-    """The streamed MXFP8 workload at full size, in the launch configuration bench.py times:
+@pytest.mark.parametrize("gemm,fmt", [("mxfp8", "e4m3"), ("mxfp4", "e2m1")])
+def test_kimi_k2_mxfp8_streamed_full_size(gemm, fmt):
+    """The streamed MXFP8 workload at full size, in the launch configuration bench.py times
+    (and the same step with MXFP4 expert GEMMs, bench.py --gemm mxfp4):
     8 micro-batches of 2048 tokens, 2-slot ring, Zipf routing, weight gradients deferred to
     the last backward call. Routing of all 16384 tokens bit-exact, and each micro-batch's
     schedule (counts, offsets, permutation, inverse, tiles) bit-exact; against the oracle's
@@ -185,11 +187,11 @@ def test_kimi_k2_mxfp8_streamed_full_size():
     sub = np.union1d(tok, tok_wr)
     exps = sorted({int(np.argmax(counts)), min(idx[tok[0]].tolist(), key=lambda e: counts[e])})
     need = set(idx[sub].ravel().tolist()) | set(exps)
-    print("case mxfp8 stream T=%d M=%d tokens %s experts %s rows %s dWr expert %d (%d rows), %d experts in the "
-          "token subset" % (w.T, M, tok.tolist(), exps, [int(counts[e]) for e in exps], e_wr, counts[e_wr],
+    print("case %s stream T=%d M=%d tokens %s experts %s rows %s dWr expert %d (%d rows), %d experts in the "
+          "token subset" % (gemm, w.T, M, tok.tolist(), exps, [int(counts[e]) for e in exps], e_wr, counts[e_wr],
                             len(need)), flush=True)
 
-    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8, mb_count=M, ring=2)
+    d = mok.Desc(w.T // M, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.DTYPES[gemm], mb_count=M, ring=2)
     q = mok.MxWeights(d, dev)
     kept = {}
     w1 = torch.empty(w.E, 2 * w.I, w.H, dtype=torch.bfloat16, device=dev)
@@ -224,7 +226,7 @@ def test_kimi_k2_mxfp8_streamed_full_size():
 
     W = _Weights(kept)
     xs, dys, wrs = x_cpu.float().numpy(), dy_cpu.float().numpy(), wr_cpu.float().numpy()
-    f, bw = oracle_step_parallel(xs[sub], W, wrs, idx[sub], g[sub], dys[sub], w.E, w.I, mx=True)
+    f, bw = oracle_step_parallel(xs[sub], W, wrs, idx[sub], g[sub], dys[sub], w.E, w.I, mx=fmt)
     pos = np.searchsorted(sub, tok)
     errs = {"y": rel_fro(np64(st.y[tok]), f["y"][pos]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"][pos]),
             "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"][pos]),
@@ -232,8 +234,8 @@ def test_kimi_k2_mxfp8_streamed_full_size():
     from concurrent.futures import ThreadPoolExecutor
 
     def one_expert(e):
-        fe = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, experts=[e])
-        return e, orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e])
+        fe = orc.mx.forward_mx(xs, W, idx, g, w.E, w.I, experts=[e], fmt=fmt)
+        return e, orc.mx.backward_mx(xs, W, wrs, idx, g, fe, dys, w.I, experts=[e], fmt=fmt)
 
     with ThreadPoolExecutor(len(exps)) as ex:
         for e, be in ex.map(one_expert, exps):
