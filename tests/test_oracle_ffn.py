@@ -243,7 +243,7 @@ def test_storage_points_hand_worked_do_rounded_before_dw2():
     assert b["dw2"][0][0, 0] == 2.0 ** -6
 
 
-@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("mx", [False, "e4m3", "e2m1"])
 def test_expert_chunked_step_equals_whole_step(mx):
     """The threaded, expert-chunked evaluation the full-size GPU tests use (harness.
     oracle_step_parallel) gives the oracle's whole-step outputs bit for bit, here with an
@@ -258,8 +258,8 @@ def test_expert_chunked_step_equals_whole_step(mx):
     z, idx, g = _route_exact(x, wr, bias, k)
     W = orc.DenseWeights(orc.bf16_round(w1), orc.bf16_round(w2))
     if mx:
-        f0 = orc.mx.forward_mx(x, W, idx, g, E, I)
-        b0 = orc.mx.backward_mx(x, W, wr, idx, g, f0, dy, I)
+        f0 = orc.mx.forward_mx(x, W, idx, g, E, I, fmt=mx)
+        b0 = orc.mx.backward_mx(x, W, wr, idx, g, f0, dy, I, fmt=mx)
     else:
         f0 = orc.forward(x, W, idx, g, "bf16", E, I)
         b0 = orc.backward(x, W, wr, idx, g, f0, dy, "bf16", I)

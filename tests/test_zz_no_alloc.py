@@ -1,7 +1,7 @@
 """mok_moe_forward_noalloc (the forward with the library's own device workspace) against
 mok_moe_forward with a caller workspace: y and the saved activations bit-identical, on
 two calls in a row, the second with a smaller batch (the shared array keeps the first
-call's contents); bf16 and streamed MXFP8; a descriptor whose workspace exceeds the
+call's contents); bf16, MXFP8 and MXFP4; a descriptor whose workspace exceeds the
 array is refused with MOK_ERR_WORKSPACE before anything is enqueued."""
 import pytest
 import torch
@@ -12,10 +12,11 @@ from mixture_experts_layer_stable_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-def _forward_both(w, case, mx=False):
+def _forward_both(w, case, gemm):
     from mixture_experts_layer_stable_amd import mok
     dev = "cuda"
-    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8 if mx else None)
+    mx = gemm != "bf16"
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.DTYPES[gemm] if mx else None)
     assert mok.workspace_query(d)["fwd_ws"] <= mok.NOALLOC_WS_BYTES
     buf = mok.Buffers(d, dev, backward=False)
     x, wr = case.x.to(dev), case.wr.to(dev)
@@ -38,13 +39,13 @@ def _forward_both(w, case, mx=False):
     assert torch.equal(buf.saved, saved_ref)
 
 
-@pytest.mark.parametrize("mx", [False, True])
-def test_noalloc_forward_matches_caller_workspace(mx):
-    big = inputs.replace(inputs.WORKLOADS["small_bf16"], gemm="mxfp8" if mx else "bf16")
+@pytest.mark.parametrize("gemm", ["bf16", "mxfp8", "mxfp4"])
+def test_noalloc_forward_matches_caller_workspace(gemm):
+    big = inputs.replace(inputs.WORKLOADS["small_bf16"], gemm=gemm)
     small = inputs.replace(big, T=300, E=12, k=3)
     for w in (big, small):
-        print("case noalloc T=%d E=%d k=%d mx=%s" % (w.T, w.E, w.k, mx), flush=True)
-        _forward_both(w, Case(w), mx)
+        print("case noalloc T=%d E=%d k=%d gemm=%s" % (w.T, w.E, w.k, gemm), flush=True)
+        _forward_both(w, Case(w), gemm)
 
 
 def test_noalloc_refuses_oversized_workspace():
