@@ -244,7 +244,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 512, "imbalanced_bf16": 512,
+    ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 2048, "imbalanced_bf16": 2048,
                                "kimi_k2_mxfp8_stream": 1}.get(w.name, 6)
     keep = cpu_sample_plan(w, ntok) if not args.no_cpu_baseline else []
     t0 = time.time()
