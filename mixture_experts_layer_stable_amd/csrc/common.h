@@ -103,11 +103,15 @@ constexpr int kHdrHash = 1, kHdrStatus = 4;
 // queue on one line: line 1 counts the XCCs that have left (word 1) and the XCC
 // arrivals at the barriers (word 2); line 2 + x counts the arrivals (word 0), the
 // workgroups (1) and the exits (2) of XCC x; line 18 + x holds the release generation
-// of XCC x; line 34 + q is work queue q (the next item to hand out). mok_schedule_build
-// zeroes them; the last workgroup to leave a fused kernel zeroes them again.
-constexpr int kSyncLine = 32, kSyncXcc = 16, kSyncQueues = 4;
+// of XCC x; line 34 + q is work queue q (the next item to hand out); line 38 + p is the
+// weight-gradient tile queue of part p (word 0: tiles handed out, word 1: workgroups that
+// have stopped claiming). mok_schedule_build zeroes them; the last workgroup to leave a
+// fused kernel zeroes them again, and the last workgroup of a part to stop claiming
+// zeroes that part's queue line.
+constexpr int kSyncLine = 32, kSyncXcc = 16, kSyncQueues = 4, kSyncDwParts = 8;
 constexpr int kSyncArrive = 2, kSyncRelease = 2 + kSyncXcc, kSyncQueue = 2 + 2 * kSyncXcc;
-constexpr int kSyncLines = kSyncQueue + kSyncQueues;
+constexpr int kSyncDw = kSyncQueue + kSyncQueues;
+constexpr int kSyncLines = kSyncDw + kSyncDwParts;
 constexpr size_t kSchedHeaderBytes = (size_t)kSyncLines * kSyncLine * 4;
 
 __device__ __forceinline__ void sync_zero(int32_t* hdr) {
@@ -119,6 +123,7 @@ __device__ __forceinline__ void sync_zero(int32_t* hdr) {
     hdr[(kSyncRelease + x) * kSyncLine] = 0;
   }
   for (int q = 0; q < kSyncQueues; ++q) hdr[(kSyncQueue + q) * kSyncLine] = 0;
+  for (int p = 0; p < kSyncDwParts; ++p) hdr[(kSyncDw + p) * kSyncLine] = hdr[(kSyncDw + p) * kSyncLine + 1] = 0;
 }
 
 struct Guard {

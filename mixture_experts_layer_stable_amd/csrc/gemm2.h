@@ -327,9 +327,16 @@ __device__ __forceinline__ void wait_vmcnt_extra(bool prologue_tile) {
   if (prologue_tile) wait_vmcnt<N + EXTRA>(); else wait_vmcnt<N>();
 }
 
-template <class Tl, int STAGES, int EXTRA, class OA, class OB>
+struct NoKtHook {
+  __device__ void operator()(int) const {}
+};
+
+// hook(kt) runs after K-tile kt's MMAs and refill DMAs are issued. A vector-memory
+// operation it issues only makes the later vmcnt waits cover more (completion is in
+// issue order), never less.
+template <class Tl, int STAGES, int EXTRA, class OA, class OB, class HK = NoKtHook>
 __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, char* smem, int wave, int lane,
-                                          f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+                                          f32x16_t (&acc)[Tl::FM][Tl::FN], HK hook = HK{}) {
   static_assert(STAGES == 3, "ring_loop waits are written for 3 stages");
   constexpr int SB = OA::BYTES + OB::BYTES;
   constexpr int NI = OA::NI + OB::NI;
@@ -340,6 +347,7 @@ __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, ch
     ring_barrier();
     const int nk = kt + STAGES - 1;
     ktile_mma<Tl>(oa, ob, smem + (kt % STAGES) * SB, nk < KT, nk, smem + (nk % STAGES) * SB, wave, acc);
+    hook(kt);
   }
   __syncthreads();
 }
@@ -412,6 +420,46 @@ __device__ __forceinline__ void dw_balanced_part(int E, int64_t TPE, F kt, int* 
                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)l));
   hi = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)h >> 32)) << 32) |
                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)h));
+}
+
+// Longest-K-first order of the experts for the weight-gradient tile queues: s_ord[i] is
+// the expert with the i-th largest K-tile count (ties by expert index), a fixed function
+// of the counts. s_kt is scratch for E ints. One rank per expert, E / blockDim passes over
+// E counts: meant for E <= kDwQueueMaxE.
+constexpr int kDwQueueMaxE = 256;
+
+template <class F>
+__device__ __forceinline__ void dw_lpt_order(int E, F kt, int* s_kt, int* s_ord) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_kt[e] = kt(e);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int v = s_kt[e];
+    int r = 0;
+    for (int f = 0; f < E; ++f) {
+      const int w = s_kt[f];
+      r += (w > v) | ((w == v) & (f < e));
+    }
+    s_ord[r] = e;
+  }
+  __syncthreads();
+}
+
+// Weight-gradient tile queue of part p (a line of the schedule header, zero at rest):
+// claim returns the part's next queue index; a workgroup that will claim no more calls
+// leave, and the part's last one zeroes the line for the next launch (no claim of this
+// launch can follow: every member has had its last claim answered).
+__device__ __forceinline__ int32_t* dw_queue_line(int32_t* hdr, int p) { return hdr + (kSyncDw + p) * kSyncLine; }
+
+__device__ __forceinline__ int dw_queue_claim(int32_t* line) {
+  return __hip_atomic_fetch_add(line, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void dw_queue_leave(int32_t* line, int members) {
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(line + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+    __hip_atomic_store(line, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(line + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // bf16 epilogue through a per-wave LDS patch: each pair of horizontally adjacent

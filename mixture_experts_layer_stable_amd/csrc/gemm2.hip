@@ -253,11 +253,25 @@ __device__ __forceinline__ void dw_tile_order(int rem, int MT, int NT, int& mt, 
 
 // Weight gradients with bf16 output, persistent and pipelined across output tiles:
 // the ring prologue of the next tile is issued before this tile's epilogue, so the
-// epilogue's stores drain while the next tile's first K-tiles load. The workgroup
-// walks a contiguous range of the tile list (e, mt, nt), one range per XCD.
+// epilogue's stores drain while the next tile's first K-tiles load.
 // When the per-wave patches fit in one ring stage they use the stage that the next
 // tile's prologue leaves free (stage STAGES-1); otherwise they follow the ring.
-template <class Tl>
+//
+// Q = false (large launches): the workgroup walks a contiguous range of the tile list
+// (e, mt, nt), one range per XCD, split by work (dw_balanced_part).
+// Q = true (launches of a few tiles per workgroup, where one expert with many rows makes
+// tiles several times longer than the others): the tiles are listed longest K first and
+// dealt round-robin to P parts (list position p goes to part p % P); a part's tiles go
+// out one at a time from its queue line in the schedule header, in list order, each
+// workgroup's first one by its index. A workgroup claims its next tile three K-tiles
+// before the end of the current one, so the claim's latency hides behind the last
+// K-tiles and the next tile's prologue still precedes this tile's epilogue. Greedy
+// longest-first assignment keeps a hot expert's tiles from queueing behind one another
+// (2048 tokens, experts 8x the mean: in a model of the walk, the busiest workgroup's
+// K-tiles 59 -> 36 for dW1, 41 -> 36 for dW2). The last workgroup of a part to stop
+// claiming zeroes the part's line for the next launch. Which workgroup computes a tile
+// never changes its bits.
+template <class Tl, bool Q>
 __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E) {
   using OA = OpMN<Tl::BM, 32, Tl::FM, Tl::NW>;
   using OB = OpMN<Tl::BN, 32, Tl::FN, Tl::NW>;
@@ -266,27 +280,52 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   constexpr int PATCH = kBf16PatchBytes;
   constexpr bool IN_RING = Tl::NW * PATCH <= SB;
   constexpr int EXTRA = Tl::FM * Tl::FN * 2;  // global stores per lane in epilogue_bf16
+  static_assert(!Q || STAGES * SB >= 4 * kDwQueueMaxE, "the ring holds the order scratch");
   __shared__ __align__(1024) char smem[STAGES * SB + (IN_RING ? 0 : Tl::NW * PATCH)];
   __shared__ int s_u[kMaxE2 + 1];
+  __shared__ int s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   char* patch = smem + (IN_RING ? (STAGES - 1) * SB : STAGES * SB) + wave * PATCH;
   const int MT = a.M / Tl::BM, NT = a.N / Tl::BN;
+  const int64_t TPE = (int64_t)MT * NT;
   const int P = min(8, (int)gridDim.x);
   const int xcd = blockIdx.x % P;
   const int nx = ((int)gridDim.x - xcd + P - 1) / P;
   const int li = blockIdx.x / P;
   if (guard_fail(a.guard)) return;
-  int64_t lo, hi;
-  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.counts[e] + 31) / 32; }, s_u, P, xcd, lo, hi);
-  int64_t L = lo + li;
-  if (L >= hi) return;
+  const auto kt_of = [&](int e) { return (a.counts[e] + 31) / 32; };
+  int32_t* qline = nullptr;
+  int64_t L, hi;
+  if constexpr (Q) {
+    dw_lpt_order(E, kt_of, reinterpret_cast<int*>(smem), s_u);
+    qline = dw_queue_line(a.guard.hdr, xcd);
+    hi = ((int64_t)E * TPE - xcd + P - 1) / P;  // this part's tiles: list positions xcd + P q, q < hi
+    L = li;
+    if (L >= hi) {
+      dw_queue_leave(qline, nx);
+      return;
+    }
+  } else {
+    int64_t lo;
+    dw_balanced_part(E, TPE, kt_of, s_u, P, xcd, lo, hi);
+    L = lo + li;
+    if (L >= hi) return;
+  }
   OA oa;
   OB ob;
   int e = 0, mt = 0, nt = 0, KT = 0;
   const auto setup = [&](int64_t l) {
-    e = __builtin_amdgcn_readfirstlane((int)(l / (MT * NT)));
-    const int rem = (int)(l - (int64_t)e * MT * NT);
+    int rem;
+    if constexpr (Q) {
+      const int64_t pos = xcd + (int64_t)P * l;
+      const int i = (int)(pos / TPE);
+      e = __builtin_amdgcn_readfirstlane(s_u[i]);
+      rem = (int)(pos - (int64_t)i * TPE);
+    } else {
+      e = __builtin_amdgcn_readfirstlane((int)(l / TPE));
+      rem = (int)(l - (int64_t)e * TPE);
+    }
     dw_tile_order(rem, MT, NT, mt, nt);
     const int seg0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
     const int cnt = __builtin_amdgcn_readfirstlane(a.counts[e]);
@@ -301,12 +340,26 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
   bool first = true;
   for (;;) {
     f32x16_t acc[Tl::FM][Tl::FN];
+    int claim = 0;  // lane 0 of wave 0: the part's next queue index
+    const int kc = KT > 3 ? KT - 3 : 0;
+    const auto hook = [&](int kt) {
+      if (Q && kt == kc && tid == 0) claim = dw_queue_claim(qline);
+    };
+    if (Q && KT == 0 && tid == 0) claim = dw_queue_claim(qline);
     if (first)
-      ring_loop<Tl, STAGES, 0>(oa, ob, KT, smem, wave, lane, acc);
+      ring_loop<Tl, STAGES, 0>(oa, ob, KT, smem, wave, lane, acc, hook);
     else
-      ring_loop<Tl, STAGES, EXTRA>(oa, ob, KT, smem, wave, lane, acc);
+      ring_loop<Tl, STAGES, EXTRA>(oa, ob, KT, smem, wave, lane, acc, hook);
     bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
-    const int64_t Ln = L + nx;
+    int64_t Ln;
+    if constexpr (Q) {
+      asm volatile("" : "+v"(claim));  // the claim is read here, after the K-loop
+      if (tid == 0) s_next = claim;
+      __syncthreads();
+      Ln = nx + (int64_t)__builtin_amdgcn_readfirstlane(s_next);
+    } else {
+      Ln = L + nx;
+    }
     if (Ln < hi) {
       setup(Ln);
       ring_prologue<STAGES>(oa, ob, KT, smem, wave);
@@ -317,6 +370,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
     L = Ln;
     first = false;
   }
+  if constexpr (Q) dw_queue_leave(qline, nx);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,7 +473,15 @@ static hipError_t dw_pipe_launch(const Ctx& c, const DwArgs2& a) {
   const int64_t tiles = (int64_t)c.E * (a.M / Tl::BM) * (a.N / Tl::BN);
   const int per_cu = Tl::BM == 128 ? 2 : 1;
   const int g = (int)std::min<int64_t>(c.grid > 0 ? c.grid : per_cu * c.num_cu, std::max<int64_t>(tiles, 1));
-  hipLaunchKernelGGL((dw_gemm2_pipe_kernel<Tl>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+  // tile queues for the 128 x 128 launches (a few tiles per workgroup), with a schedule
+  // header to hold them
+  if constexpr (Tl::BM == 128) {
+    if (c.E <= kDwQueueMaxE && a.guard.hdr != nullptr) {
+      hipLaunchKernelGGL((dw_gemm2_pipe_kernel<Tl, true>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((dw_gemm2_pipe_kernel<Tl, false>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
   return hipGetLastError();
 }
 

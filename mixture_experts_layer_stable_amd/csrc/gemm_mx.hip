@@ -136,9 +136,11 @@ __device__ __forceinline__ void mx_ring_prologue(const OA& oa, const OB& ob, con
   }
 }
 
-template <int F, class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB>
+// hook(kt) runs after K-tile kt's MMAs and refill DMAs are issued (as in ring_loop).
+template <int F, class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB, class HK = NoKtHook>
 __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
-                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
+                                             char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN],
+                                             HK hook = HK{}) {
   static_assert(STAGES == 3, "the waits are written for 3 stages");
   constexpr int SD = MxFmt<F>::SD;
   constexpr int OFF_B = OA::BYTES, OFF_SA = OA::BYTES + OB::BYTES, OFF_SB = OFF_SA + SA::BYTES;
@@ -177,6 +179,7 @@ __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const S
       mx_kstep<F, 2, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
       mx_kstep<F, 3, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
     }
+    hook(kt);
   }
   __syncthreads();
 }
@@ -391,11 +394,14 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_kernel(MxDwArgs a) {
 }
 
 // Persistent form of dw_mx_kernel for bf16 gradients (the same tiles and arithmetic):
-// a workgroup walks tiles L = lo + li, lo + li + nx, ... of its XCD's contiguous part
-// of the (expert, M-tile, N-tile) range; the next tile's first K-tiles are issued
-// before this tile's epilogue, whose stores then drain under the next K-loop. The
-// epilogue's per-wave patches use the ring stage that this prologue leaves free.
-template <class Tl, int F>
+// the next tile's first K-tiles are issued before this tile's epilogue, whose stores
+// then drain under the next K-loop. The epilogue's per-wave patches use the ring stage
+// that this prologue leaves free. Q = false: a workgroup walks tiles L = lo + li,
+// lo + li + nx, ... of its XCD's contiguous part of the (expert, M-tile, N-tile) range
+// (hundreds of tiles per workgroup at the streamed Kimi-K2 shape, where a hot expert's
+// tile is a small share of a workgroup's work). Q = true (launches of a few tiles per
+// workgroup): longest-K-first tile queues, as in the bf16 weight-gradient kernel.
+template <class Tl, int F, bool Q>
 __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   using Fm = MxFmt<F>;
   using OA = OpK<Tl::BM, Tl::FM, Tl::NW>;
@@ -416,12 +422,26 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   const int xcd = blockIdx.x % P;
   const int nx = ((int)gridDim.x - xcd + P - 1) / P;
   const int li = blockIdx.x / P;
+  const int64_t TPE = (int64_t)MT * NT;
   if (guard_fail(a.guard)) return;
-  int64_t lo, hi;
-  dw_balanced_part(E, (int64_t)MT * NT, [&](int e) { return (a.pofs[e + 1] - a.pofs[e]) / Fm::KTILE; }, s_u, P,
-                   xcd, lo, hi);
-  int64_t L = lo + li;
-  if (L >= hi) return;
+  const auto kt_of = [&](int e) { return (a.pofs[e + 1] - a.pofs[e]) / Fm::KTILE; };
+  int32_t* qline = nullptr;
+  int64_t L, hi;
+  if constexpr (Q) {
+    dw_lpt_order(E, kt_of, reinterpret_cast<int*>(smem), s_u);
+    qline = dw_queue_line(a.guard.hdr, xcd);
+    hi = ((int64_t)E * TPE - xcd + P - 1) / P;  // this part's tiles: list positions xcd + P q, q < hi
+    L = li;
+    if (L >= hi) {
+      dw_queue_leave(qline, nx);
+      return;
+    }
+  } else {
+    int64_t lo;
+    dw_balanced_part(E, TPE, kt_of, s_u, P, xcd, lo, hi);
+    L = lo + li;
+    if (L >= hi) return;
+  }
   const auto frow_a = [&](int f) { return wm * Tl::WTM + f * 32; };
   const auto frow_b = [&](int f) { return wn * Tl::WTN + f * 32; };
   OA oa;
@@ -431,8 +451,16 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   int e = 0, mt = 0, nt = 0, KT = 0;
   const int64_t ldq = Fm::bytes(a.kld);
   const auto setup = [&](int64_t l) {
-    e = __builtin_amdgcn_readfirstlane((int)(l / (MT * NT)));
-    const int rem = (int)(l - (int64_t)e * MT * NT);
+    int rem;
+    if constexpr (Q) {
+      const int64_t pos = xcd + (int64_t)P * l;
+      const int i = (int)(pos / TPE);
+      e = __builtin_amdgcn_readfirstlane(s_u[i]);
+      rem = (int)(pos - (int64_t)i * TPE);
+    } else {
+      e = __builtin_amdgcn_readfirstlane((int)(l / TPE));
+      rem = (int)(l - (int64_t)e * TPE);
+    }
     mt = __builtin_amdgcn_readfirstlane(rem / NT);
     nt = __builtin_amdgcn_readfirstlane(rem - mt * NT);
     const int64_t k0 = __builtin_amdgcn_readfirstlane(a.pofs[e]);
@@ -451,12 +479,27 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
   bool first = true;
   for (;;) {
     f32x16_t acc[Tl::FM][Tl::FN];
+    int claim = 0;  // lane 0 of wave 0: the part's next queue index
+    const int kc = KT > 2 ? KT - 2 : 0;  // K-tiles of 128 (256) rows: two hide the claim
+    const auto hook = [&](int kt) {
+      if (Q && kt == kc && tid == 0) claim = dw_queue_claim(qline);
+    };
+    if (Q && KT == 0 && tid == 0) claim = dw_queue_claim(qline);
     if (first)
-      mx_ring_loop<F, Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+      mx_ring_loop<F, Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
     else
-      mx_ring_loop<F, Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc);
+      mx_ring_loop<F, Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
     bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
-    const int64_t Ln = L + nx;
+    int64_t Ln;
+    if constexpr (Q) {
+      __shared__ int s_next;
+      asm volatile("" : "+v"(claim));  // the claim is read here, after the K-loop
+      if (tid == 0) s_next = claim;
+      __syncthreads();
+      Ln = nx + (int64_t)__builtin_amdgcn_readfirstlane(s_next);
+    } else {
+      Ln = L + nx;
+    }
     if (Ln < hi) {
       setup(Ln);
       mx_ring_prologue<STAGES>(oa, ob, sa, sb, KT, smem, wave);
@@ -467,6 +510,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
     L = Ln;
     first = false;
   }
+  if constexpr (Q) dw_queue_leave(qline, nx);
 }
 
 // ---------------------------------------------------------------------------
@@ -565,10 +609,19 @@ static hipError_t dw_launch_mx(const Ctx& c, const MxDwArgs& a) {
   if (blocks == 0) return hipSuccess;
   if (!c.wgrad_f32) {
     const int g = (int)std::min<int64_t>(c.grid > 0 ? c.grid : c.num_cu, blocks);
-    if (c.mx4)
-      hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 1>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
-    else
-      hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 0>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    // tile queues when the launch has a few tiles per workgroup
+    const bool q = blocks <= 16 * (int64_t)g && c.E <= kDwQueueMaxE && a.guard.hdr != nullptr;
+    if (c.mx4) {
+      if (q)
+        hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 1, true>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+      else
+        hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 1, false>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    } else {
+      if (q)
+        hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 0, true>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+      else
+        hipLaunchKernelGGL((dw_mx_pipe_kernel<Tl, 0, false>), dim3(g), dim3(Tl::NT), 0, c.s, a, c.E);
+    }
     return hipGetLastError();
   }
   if (c.mx4)

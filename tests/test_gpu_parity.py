@@ -211,6 +211,52 @@ def test_bit_reproducible_across_runs_tiles_and_grids(name):
                                ref[key].view(torch.int16) if ref[key].dtype == torch.bfloat16 else ref[key]), (kw, key)
 
 
+@pytest.mark.parametrize("gemm", ["bf16", "mxfp8"])
+def test_dw_tile_queues_reset_between_launches(gemm):
+    """Weight-gradient launches with a few tiles per workgroup (here: 2048 tokens, Zipf
+    routing) hand their tiles out from counters in the schedule header (lines 38-45 of 128
+    bytes; word 0 counts tiles handed out, word 1 workgroups done), which each launch's
+    last workgroup zeroes again. Three backwards in a row on the same buffers, each with
+    another dY and its outputs pre-filled with NaN, equal one-shot runs on fresh buffers
+    bit for bit, and the counters read zero after each."""
+    from mixture_experts_layer_stable_amd import mok
+    w = inputs.WORKLOADS["imbalanced_bf16"]
+    dev = "cuda"
+    x, wr, dy0 = inputs.make_x(w).to(dev), inputs.make_wr(w).to(dev), inputs.make_dy(w).to(dev)
+    b = inputs.make_bias(w)
+    b = None if b is None else b.to(dev)
+    w1 = torch.stack([inputs.make_w1(w, e) for e in range(w.E)]).to(dev)
+    w2 = torch.stack([inputs.make_w2(w, e) for e in range(w.E)]).to(dev)
+    d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16, gemm=mok.MXFP8 if gemm == "mxfp8" else mok.BF16)
+    q = None
+    if gemm == "mxfp8":
+        q = mok.MxWeights(d, dev)
+        mok.weights_quantize(d, w1, w2, q)
+    names = ("y", "dx", "dgate", "dw1", "dw2", "dwr")
+
+    def run(buf, dy):
+        for n in names:
+            getattr(buf, n).fill_(float("nan"))
+        mok.step(d, buf, x, wr, b, None if q else w1, None if q else w2, dy, mxw=q)
+        torch.cuda.synchronize()
+        mok.check_schedule(d, buf.sched, "step")
+        lines = buf.sched[38 * 128: 46 * 128].view(torch.int32).view(8, 32)[:, :2]
+        assert torch.all(lines == 0), lines.cpu()
+        return {n: getattr(buf, n).clone() for n in names}
+
+    same = mok.Buffers(d, dev)
+    for j in range(3):
+        dy = torch.roll(dy0, 7 * j, 0)
+        print("case", gemm, "backward", j, flush=True)
+        got = run(same, dy)
+        ref = run(mok.Buffers(d, dev), dy)
+        for n in names:
+            a, c = got[n], ref[n]
+            assert not torch.isnan(a.float()).any(), (j, n)
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               c.view(torch.int16) if c.dtype == torch.bfloat16 else c), (j, n)
+
+
 def test_schedule_built_for_another_descriptor_is_rejected():
     """A schedule built for one descriptor and handed to forward/backward with another: every
     kernel checks the header's descriptor hash first, so nothing is written (outputs keep
