@@ -641,15 +641,20 @@ mok_status mok_moe_backward(const mok_desc* d, void* sched, const void* x, const
     MOK_LAUNCH("dx_reduce", c.s, launch_dx_reduce(c, wb + L.bpart, dz, idx, wr, dx));
   }
   if (c.act == MOK_BF16) {
+    // routed-order operands of the weight gradients: dO = bf16(g * dY) rows by a gather; the
+    // x rows by the router-weight gradient, which reads each of them once (else a gather)
     MOK_LAUNCH("gather", c.s, launch_gather_rows(c, dy, gate, wb + L.dos));
-    MOK_LAUNCH("gather", c.s, launch_gather_rows(c, x, nullptr, wb + L.xs));
+    if (dwr != nullptr)
+      MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr, wb + L.xs));
+    else
+      MOK_LAUNCH("gather", c.s, launch_gather_rows(c, x, nullptr, wb + L.xs));
     MOK_LAUNCH("dw2", c.s, launch_dw2_bf16(c, wb + L.dos, hr, dw2));
     MOK_LAUNCH("dw1", c.s, launch_dw1_bf16(c, wb + L.dgu, wb + L.xs, dw1));
   } else {
     MOK_LAUNCH("dw2", c.s, launch_dw2(c, dy, gate, hr, dw2));
     MOK_LAUNCH("dw1", c.s, launch_dw1(c, wb + L.dgu, x, dw1));
+    if (dwr != nullptr) MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr, nullptr));
   }
-  if (dwr != nullptr) MOK_LAUNCH("dwr", c.s, launch_dwr(c, dz, x, dwr));
   return MOK_OK;
 }
 

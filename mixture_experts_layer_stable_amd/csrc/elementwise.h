@@ -93,10 +93,13 @@ __device__ __forceinline__ void dx_reduce_body(const T* __restrict__ part, const
 // 64 lanes x 4 vectors for H <= 2048 (2048 tokens, Zipf: 18 -> 13 us), 32 lanes x 8
 // vectors (whole 128-byte row pieces) above (Kimi-K2 shape: 0.33 ms, against 0.56 with
 // 64 x 4). red: kDwrLanes x (kDwrVec * VE + 1) floats of LDS.
+// xs (nullptr: not written): routed-order copy of the x rows, xs[r] = x[perm[r] / k], for the
+// dW1 GEMM; every (row, vector) of x is read by exactly one thread here.
 template <typename T, typename TO, int kDwrVec, int kDwrLanes>
 __device__ __forceinline__ void dwr_body(const float* __restrict__ dz, const T* __restrict__ x,
                                          const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                                         TO* __restrict__ dwr, int E, int H, int k, int item, float* red) {
+                                         TO* __restrict__ dwr, int E, int H, int k, int item, float* red,
+                                         T* __restrict__ xs = nullptr) {
   constexpr int VE = Elem<T>::VE;
   constexpr int COLS = kDwrVec * VE;
   const int vpr = H / VE;
@@ -109,13 +112,43 @@ __device__ __forceinline__ void dwr_body(const float* __restrict__ dz, const T* 
   for (int q = 0; q < VE; ++q) acc[q] = 0.0f;
   if (v < vpr) {
     const int r1 = offsets[e + 1];
-    for (int r = offsets[e] + rl; r < r1; r += kDwrLanes) {
-      const int s = perm[r];
-      const float d = dz[s];
-      float f[VE];
-      unpack(ldg16(x + (int64_t)(s / k) * H + v * VE), f, (T*)nullptr);
+    if (xs == nullptr) {
+      for (int r = offsets[e] + rl; r < r1; r += kDwrLanes) {
+        const int s = perm[r];
+        const float d = dz[s];
+        float f[VE];
+        unpack(ldg16(x + (int64_t)(s / k) * H + v * VE), f, (T*)nullptr);
 #pragma unroll
-      for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+        for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d, f[q], acc[q]);
+      }
+    } else {
+      // rows in groups of 4: the group's loads go out before its copies are stored, so a
+      // load waits behind the previous group's stores only (vmcnt counts both in order)
+      constexpr int G = 4;
+      for (int r = offsets[e] + rl; r < r1; r += G * kDwrLanes) {
+        uint4 raw[G];
+        float d[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int rr = r + g * kDwrLanes;
+          const int s = rr < r1 ? perm[rr] : 0;
+          d[g] = rr < r1 ? dz[s] : 0.0f;
+          raw[g] = rr < r1 ? ldg16(x + (int64_t)(s / k) * H + v * VE) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int rr = r + g * kDwrLanes;
+          if (rr < r1) {
+            typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+            const u32x4_t w = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(xs + (int64_t)rr * H + v * VE));
+            float f[VE];
+            unpack(raw[g], f, (T*)nullptr);
+#pragma unroll
+            for (int q = 0; q < VE; ++q) acc[q] = __builtin_fmaf(d[g], f[q], acc[q]);
+          }
+        }
+      }
     }
   }
 #pragma unroll

@@ -49,10 +49,11 @@ __global__ __launch_bounds__(kDwrVec * kDwrLanes) void dwr_kernel(Guard gd, cons
                                                                   const T* __restrict__ x,
                                                                   const int32_t* __restrict__ offsets,
                                                                   const int32_t* __restrict__ perm,
-                                                                  TO* __restrict__ dwr, int E, int H, int k) {
+                                                                  TO* __restrict__ dwr, int E, int H, int k,
+                                                                  T* __restrict__ xs) {
   __shared__ float red[kDwrLanes * (kDwrVec * Elem<T>::VE + 1)];
   if (guard_fail(gd)) return;
-  dwr_body<T, TO, kDwrVec, kDwrLanes>(dz, x, offsets, perm, dwr, E, H, k, (int)blockIdx.x, red);
+  dwr_body<T, TO, kDwrVec, kDwrLanes>(dz, x, offsets, perm, dwr, E, H, k, (int)blockIdx.x, red, xs);
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(Guard gd, const bf16* __restrict__ src,
@@ -109,26 +110,26 @@ hipError_t launch_dx_reduce(const Ctx& c, const void* part, const float* dz, con
 }
 
 template <int VEC, int LANES>
-static hipError_t launch_dwr_shape(const Ctx& c, const float* dz, const void* x, void* dwr) {
+static hipError_t launch_dwr_shape(const Ctx& c, const float* dz, const void* x, void* dwr, void* xs) {
   const int ve = c.act == MOK_F32 ? 4 : 8;
   const int64_t nvb = ((int64_t)(c.H / ve) + VEC - 1) / VEC;
   const dim3 grid((unsigned)(c.E * nvb)), block(VEC * LANES);
   if (c.E * nvb == 0) return hipSuccess;
   if (c.act == MOK_F32) {
     hipLaunchKernelGGL((dwr_kernel<float, float, VEC, LANES>), grid, block, 0, c.s, c.guard, dz, (const float*)x, c.offsets,
-                       c.perm, (float*)dwr, c.E, c.H, c.k);
+                       c.perm, (float*)dwr, c.E, c.H, c.k, (float*)nullptr);
   } else if (c.wgrad_f32) {
     hipLaunchKernelGGL((dwr_kernel<bf16, float, VEC, LANES>), grid, block, 0, c.s, c.guard, dz, (const bf16*)x, c.offsets,
-                       c.perm, (float*)dwr, c.E, c.H, c.k);
+                       c.perm, (float*)dwr, c.E, c.H, c.k, (bf16*)xs);
   } else {
     hipLaunchKernelGGL((dwr_kernel<bf16, bf16, VEC, LANES>), grid, block, 0, c.s, c.guard, dz, (const bf16*)x, c.offsets,
-                       c.perm, (bf16*)dwr, c.E, c.H, c.k);
+                       c.perm, (bf16*)dwr, c.E, c.H, c.k, (bf16*)xs);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr) {
-  return c.H <= 2048 ? launch_dwr_shape<4, 64>(c, dz, x, dwr) : launch_dwr_shape<8, 32>(c, dz, x, dwr);
+hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr, void* xs) {
+  return c.H <= 2048 ? launch_dwr_shape<4, 64>(c, dz, x, dwr, xs) : launch_dwr_shape<8, 32>(c, dz, x, dwr, xs);
 }
 
 }  // namespace mok

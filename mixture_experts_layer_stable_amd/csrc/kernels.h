@@ -50,7 +50,8 @@ hipError_t launch_dx_reduce(const Ctx& c, const void* part, const float* dz, con
                             void* dx);
 hipError_t launch_dw2(const Ctx& c, const void* dy, const float* gate, const void* h, void* dw2);
 hipError_t launch_dw1(const Ctx& c, const void* dgu, const void* x, void* dw1);
-hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr);
+// xs (bf16 only; nullptr: not written): the routed-order copy of the x rows for dW1
+hipError_t launch_dwr(const Ctx& c, const float* dz, const void* x, void* dwr, void* xs);
 
 // bf16 grouped GEMMs on the direct-to-LDS core
 hipError_t launch_fc1_bf16(const Ctx& c, const void* x, const void* w1, void* au, void* h);
