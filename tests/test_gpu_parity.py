@@ -89,15 +89,18 @@ def test_tiny_fp32_backward_parity():
     _full(w)
 
 
-@pytest.mark.parametrize("T", [3000, 5000, 9000, 17000])
-def test_route_token_group_sizes(T):
+@pytest.mark.parametrize("T,E", [(3000, 72), (5000, 72), (9000, 72), (17000, 72), (1000, 20), (3000, 20),
+                                 (9000, 6), (777, 13)])
+def test_route_token_group_sizes(T, E):
     """The router picks 4, 8, 16 or 32 tokens per workgroup by batch size (3000, 5000, 9000
-    and 17000 tokens select each of them on 256 compute units; the last group is ragged):
-    logits and indices equal the oracle's bit for bit, gates within 1e-6."""
+    and 17000 tokens select each of them on 256 compute units for 72 experts; the last group
+    is ragged); with at most 32 experts a wave holds tokens x experts, one or two chains per
+    lane (1000 / 3000 tokens of 20 experts, 9000 of 6, a ragged 777 of 13): logits and
+    indices equal the oracle's bit for bit, gates within 1e-6."""
     import oracle as orc
     from mixture_experts_layer_stable_amd import mok
 
-    w = _w("imbalanced_bf16", T=T, E=72, k=3, H=256, I=128)
+    w = _w("imbalanced_bf16", T=T, E=E, k=3, H=256, I=128)
     print("case T=%d E=%d k=%d H=%d" % (w.T, w.E, w.k, w.H), flush=True)
     x, wr, b = inputs.make_x(w), inputs.make_wr(w), inputs.make_bias(w)
     d = mok.Desc(w.T, w.H, w.E, w.k, w.I, act=mok.BF16)
