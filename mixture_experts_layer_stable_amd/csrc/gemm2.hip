@@ -235,22 +235,6 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_kernel(DwArgs2 a) {
   dw_gemm2_body<Tl, TO>(a, smem, xcd_logical(blockIdx.x, gridDim.x));
 }
 
-// Order of an expert's output tiles in the persistent weight-gradient walk: blocks of
-// kDwBandGroup row bands, column-major inside a block, so the 32 tiles an XCD works on at
-// once share 4 row bands of A and 8 column bands of B (about 2 MB at the Kimi-K2 shape,
-// which the XCD's 4 MB L2 keeps); B is then fetched once per block instead of once per
-// row band (dW1 HBM reads 26.2 -> 8.5 GB per launch at the Kimi-K2 shape, same time;
-// 8-band blocks read 5.3 GB but ran 3.5 % slower). Which tile a workgroup takes never
-// changes its bits.
-constexpr int kDwBandGroup = 4;
-
-__device__ __forceinline__ void dw_tile_order(int rem, int MT, int NT, int& mt, int& nt) {
-  const int b = rem / (kDwBandGroup * NT), gm = min(kDwBandGroup, MT - b * kDwBandGroup);
-  const int r = rem - b * kDwBandGroup * NT, c = r / gm;
-  nt = __builtin_amdgcn_readfirstlane(c);
-  mt = __builtin_amdgcn_readfirstlane(b * kDwBandGroup + (r - c * gm));
-}
-
 // Weight gradients with bf16 output, persistent and pipelined across output tiles:
 // the ring prologue of the next tile is issued before this tile's epilogue, so the
 // epilogue's stores drain while the next tile's first K-tiles load.

@@ -461,8 +461,7 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
       e = __builtin_amdgcn_readfirstlane((int)(l / TPE));
       rem = (int)(l - (int64_t)e * TPE);
     }
-    mt = __builtin_amdgcn_readfirstlane(rem / NT);
-    nt = __builtin_amdgcn_readfirstlane(rem - mt * NT);
+    dw_tile_order(rem, MT, NT, mt, nt);
     const int64_t k0 = __builtin_amdgcn_readfirstlane(a.pofs[e]);
     KT = __builtin_amdgcn_readfirstlane((int)((a.pofs[e + 1] - k0) / Fm::KTILE));
     oa.init(a.aq + (int64_t)mt * Tl::BM * ldq + Fm::bytes(k0), [&](int r) -> uint32_t { return (uint32_t)(r * ldq); },
