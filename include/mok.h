@@ -112,8 +112,8 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2, MOK_MXFP4 = 3
                                    workgroup per compute unit, separated by grid barriers
                                    whose words live in the schedule buffer. Same arithmetic
                                    and bits as the separate kernels. Requires act = gemm =
-                                   MOK_BF16, a 32-row schedule tile (the two-wave rule picks
-                                   it below about 16k routed rows, or tile_m = 32),
+                                   MOK_BF16, a 32-row schedule tile (tile_m = 0 picks it with
+                                   this flag, or tile_m = 32),
                                    k * I / 32 <= 2048 and no MOK_FLAG_WGRAD_F32: else
                                    MOK_ERR_SHAPE or MOK_ERR_DTYPE. The workgroups must be
                                    resident together: no other kernel may hold compute units
@@ -128,8 +128,8 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2, MOK_MXFP4 = 3
  * act = MOK_BF16 (anything else: MOK_ERR_DTYPE); MOK_MXFP4 needs H and I multiples
  * of 256 (else MOK_ERR_SHAPE).
  * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile
- *   that still gives every grouped GEMM at least two full waves of the
- *   GPU's compute units.
+ *   for which the FC1 GEMM has at least one full wave of tiles (one per compute
+ *   unit) even if every row went to one expert; 32 with MOK_FLAG_FUSED.
  * grid: workgroups of the persistent GEMM kernels; 0 = one wave of the GPU.
  * Micro-batch streaming (MX only; bf16/fp32 need mb_count <= 1): one step is
  *   mb_count micro-batches of T tokens each, forward in any order and backward in
