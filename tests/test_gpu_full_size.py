@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle as orc
-from harness import TOL, np64, oracle_step_parallel, rel_fro
+from harness import ROW_TOL, TOL, np64, oracle_step_parallel, rel_fro, rel_fro_rows
 from mixture_experts_layer_stable_amd import inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -125,6 +125,12 @@ def _run(w):
         "dgate": rel_fro(buf.dgate[tok].cpu().numpy(), bwd["dgate"][pos]),
         "dwr[%d]" % e_wr: rel_fro(np64(buf.dwr[e_wr]), bwd["dwr"][e_wr]),
     }
+    rows_err = {
+        "y": rel_fro_rows(np64(buf.y[tok]), fwd["y"][pos]),
+        "h": rel_fro_rows(np64(saved["h"][rows]), fwd["h"][srow]),
+        "dx": rel_fro_rows(np64(buf.dx[tok]), bwd["dx"][pos]),
+        "dwr[%d]" % e_wr: rel_fro_rows(np64(buf.dwr[e_wr]), bwd["dwr"][e_wr]),
+    }
 
     # ---- sampled experts: whole dW1[e], dW2[e] over all of e's rows (all tokens), one thread each
     from concurrent.futures import ThreadPoolExecutor
@@ -138,9 +144,14 @@ def _run(w):
         for e, b_e in ex.map(one_expert, exps):
             errs["dw1[%d]" % e] = rel_fro(np64(buf.dw1[e]), b_e["dw1"][e])
             errs["dw2[%d]" % e] = rel_fro(np64(buf.dw2[e]), b_e["dw2"][e])
+            rows_err["dw1[%d]" % e] = rel_fro_rows(np64(buf.dw1[e]), b_e["dw1"][e])
+            rows_err["dw2[%d]" % e] = rel_fro_rows(np64(buf.dw2[e]), b_e["dw2"][e])
     print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    print("largest row error:", {k: "%.2e" % v for k, v in rows_err.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL["bf16"], (k, v)
+    for k, v in rows_err.items():
+        assert v <= ROW_TOL["bf16"], ("row", k, v)
 
     # ---- reproducibility: a second step gives the same bits
     ref = {n: getattr(buf, n).clone() for n in ("y", "dx", "dw1", "dw2", "dwr", "dgate", "gate")}
@@ -231,6 +242,8 @@ def test_kimi_k2_mxfp8_streamed_full_size(gemm, fmt):
     errs = {"y": rel_fro(np64(st.y[tok]), f["y"][pos]), "dx": rel_fro(np64(st.dx[tok]), bw["dx"][pos]),
             "dgate": rel_fro(st.dgate[tok].cpu().numpy(), bw["dgate"][pos]),
             "dwr[%d]" % e_wr: rel_fro(np64(st.dwr[e_wr]), bw["dwr"][e_wr])}
+    rows_err = {"y": rel_fro_rows(np64(st.y[tok]), f["y"][pos]), "dx": rel_fro_rows(np64(st.dx[tok]), bw["dx"][pos]),
+                "dwr[%d]" % e_wr: rel_fro_rows(np64(st.dwr[e_wr]), bw["dwr"][e_wr])}
     from concurrent.futures import ThreadPoolExecutor
 
     def one_expert(e):
@@ -241,9 +254,14 @@ def test_kimi_k2_mxfp8_streamed_full_size(gemm, fmt):
         for e, be in ex.map(one_expert, exps):
             errs["dw1[%d]" % e] = rel_fro(np64(st.dw1[e]), be["dw1"][e])
             errs["dw2[%d]" % e] = rel_fro(np64(st.dw2[e]), be["dw2"][e])
+            rows_err["dw1[%d]" % e] = rel_fro_rows(np64(st.dw1[e]), be["dw1"][e])
+            rows_err["dw2[%d]" % e] = rel_fro_rows(np64(st.dw2[e]), be["dw2"][e])
     print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    print("largest row error:", {k: "%.2e" % v for k, v in rows_err.items()}, flush=True)
     for k, v in errs.items():
         assert v <= 2e-2, (k, v)
+    for k, v in rows_err.items():  # every single row, as in the small MX parity tests
+        assert v <= 0.15, ("row", k, v)
 
     ref = {n: getattr(st, n).clone() for n in ("y", "dx", "dw1", "dw2", "dwr", "dgate")}
     st.run(x, wr, bias, q, dy)

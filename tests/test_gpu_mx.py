@@ -14,12 +14,16 @@ import pytest
 import torch
 
 import oracle as orc
-from harness import np64, rel_fro
+from harness import np64, rel_fro, rel_fro_rows
 from mixture_experts_layer_stable_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
 TOL_MX = 2e-2
+# every single row (last-axis vector) of an output: a row holds few elements and one
+# quantisation decision taken differently at a near-tie (fp32 against the oracle's fp64
+# inputs to a quantiser) moves it by up to an element step; largest measured 7.4e-2
+ROW_TOL_MX = 0.15
 DEV = "cuda"
 
 
@@ -157,6 +161,17 @@ def test_mx_step_parity(name, tile_m):
     print("rel. Frobenius:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL_MX, (k, v)
+    rows = {
+        "y": rel_fro_rows(np64(g["y"]), f["y"]),
+        "h": rel_fro_rows(np64(g["h"]), f["h"][perm]),
+        "dx": rel_fro_rows(np64(g["dx"]), bw["dx"]),
+        "dw1": rel_fro_rows(np64(g["dw1"]), np.stack([bw["dw1"][e] for e in range(w.E)])),
+        "dw2": rel_fro_rows(np64(g["dw2"]), np.stack([bw["dw2"][e] for e in range(w.E)])),
+        "dwr": rel_fro_rows(np64(g["dwr"]), bw["dwr"]),
+    }
+    print("largest row error:", {k: "%.2e" % v for k, v in rows.items()}, flush=True)
+    for k, v in rows.items():
+        assert v <= ROW_TOL_MX, ("row", k, v)
 
 
 def test_mx_streamed_equals_whole_batch():

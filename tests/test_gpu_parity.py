@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import TOL, Case, np64, rel_fro, run_gpu, run_oracle
+from harness import ROW_TOL, TOL, Case, np64, rel_fro, rel_fro_rows, run_gpu, run_oracle
 from mixture_experts_layer_stable_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -36,15 +36,22 @@ def _check_routing(g, o):
     np.testing.assert_array_equal(g["tile_start"][-1], len(sc["tiles"]))
 
 
+def _check_rows(pairs, row_tol):
+    """Every row of every output within row_tol (see harness.ROW_TOL)."""
+    rows = {n: rel_fro_rows(np64(a), r) for n, (a, r) in pairs.items()}
+    for n, e in rows.items():
+        assert e <= row_tol, ("row", n, e, rows)
+
+
 def _check_forward(w, g, o, tol):
     fwd = o["fwd"]
     perm = o["sched"]["perm"]
-    errs = {"y": rel_fro(np64(g["y"]), fwd["y"]),
-            "a": rel_fro(np64(g["a"]), fwd["a"][perm]),
-            "u": rel_fro(np64(g["u"]), fwd["u"][perm]),
-            "h": rel_fro(np64(g["h"]), fwd["h"][perm])}
+    pairs = {"y": (g["y"], fwd["y"]), "a": (g["a"], fwd["a"][perm]), "u": (g["u"], fwd["u"][perm]),
+             "h": (g["h"], fwd["h"][perm])}
+    errs = {n: rel_fro(np64(a), r) for n, (a, r) in pairs.items()}
     for n, e in errs.items():
         assert e <= tol, (n, e, errs)
+    _check_rows(pairs, ROW_TOL[w.act] if tol == TOL[w.act] else 4 * tol)
     return errs
 
 
@@ -56,10 +63,13 @@ def _check_backward(w, g, o, tol, router=True):
             "dw1": rel_fro(np64(g["dw1"]), dw1),
             "dw2": rel_fro(np64(g["dw2"]), dw2),
             "dgate": rel_fro(g["dgate"], b["dgate"])}
+    pairs = {"dx": (g["dx"], b["dx"]), "dw1": (g["dw1"], dw1), "dw2": (g["dw2"], dw2)}
     if router:
         errs["dwr"] = rel_fro(np64(g["dwr"]), b["dwr"])
+        pairs["dwr"] = (g["dwr"], b["dwr"])
     for n, e in errs.items():
         assert e <= tol, (n, e, errs)
+    _check_rows(pairs, ROW_TOL[w.act] if tol == TOL[w.act] else 4 * tol)
     return errs
 
 
