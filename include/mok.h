@@ -196,8 +196,10 @@ typedef struct mok_sizes {
 } mok_sizes;
 
 /* Byte offsets of the schedule table's parts inside the schedule buffer.
- * (After the header come the grid-barrier words of MOK_FLAG_FUSED, and after the
- * tiles the build's scratch; neither is listed here.)
+ * (After the header come the grid-barrier words of MOK_FLAG_FUSED and the counters
+ * of the weight-gradient tile queues, and after the tiles the build's scratch; none
+ * is listed here. Those words are zero between calls; two calls that use one schedule
+ * buffer must not overlap in time.)
  *   header int32[16] at offset 0: [0] 0x4D4F4B53, [1] descriptor hash, [2] tile
  *                              height, [3] tile capacity, [4] status (MOK_OK after
  *                              mok_schedule_build; MOK_ERR_SCHEDULE_MISMATCH once a
