@@ -46,6 +46,44 @@ STEP_ROOFLINE_MS = {"small_bf16": 0.058, "imbalanced_bf16": 0.058, "kimi_k2_bf16
                     "kimi_k2_mxfp8_stream": 41.0, "kimi_k2_mxfp8_stream/mxfp4": 26.2}
 
 
+def copy_ceiling_gbs(torch):
+    """Measured HBM ceiling: a 1 GiB device-to-device copy (bytes read + written over its
+    best time of three)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        best = t if best is None else min(best, t)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / (best * 1e-3) / 1e9
+
+
+HBM_KERNELS = ("route", "schedule", "combine", "router_bwd", "dx_reduce", "gather", "dwr")
+
+
+def hbm_kernels(w, per, copy_gbs):
+    """The bandwidth-bound kernels of the step: algorithmic bytes per step over their
+    summed time in the per-kernel breakdown, against 8 TB/s and against the measured
+    copy ceiling. (Streamed MX steps: the per-micro-batch kernels only.)"""
+    M = max(1, w.micro_batches)
+    out = {"copy_ceiling_gbs": round(copy_gbs, 1)}
+    for name in HBM_KERNELS:
+        if name not in per or per[name] <= 0 or (M > 1 and name in ("dwr", "gather")):
+            continue
+        nb = kernel_work(w, name)[1] * M
+        gbs = nb / (per[name] * 1e-3) / 1e9
+        out[name] = {"ms": round(per[name], 4), "gb": round(nb / 1e9, 4), "gbs": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 3), "frac_of_copy": round(gbs / copy_gbs, 3)}
+    return out
+
+
 def launch_flops(w, name):
     """Flops of one launch of an expert GEMM (row GEMMs: one micro-batch; dW: the step)."""
     M = max(1, w.micro_batches)
@@ -88,7 +126,9 @@ def kernel_work(w, name, active_experts=None):
         return "mfma", flops[name]
     nbytes = {"combine": R * H * es + T * H * es + 4 * R,
               "dx_reduce": R * H * es + T * H * es + 8 * R + R * H * es,
-              "dwr": R * H * es + E * H * es + 8 * R,
+              # bf16: dWr also writes the routed-order x rows that dW1 reads
+              "dwr": R * H * es + E * H * es + 8 * R + (R * H * es if w.act == "bf16" else 0),
+              "gather": 2 * R * H * es + 8 * R,  # routed-order dO = g*dY rows for dW2
               "router_bwd": 4 * R * (I // 256 + 4),
               "route": T * H * es + E * H * es + 8 * R,
               "schedule": 4 * R * (2 * E // 64 + 2)}
@@ -244,6 +284,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    copy_gbs = copy_ceiling_gbs(torch)
     ntok = args.cpu_tokens or {"tiny_fp32": 64, "small_bf16": 2048, "imbalanced_bf16": 2048,
                                "kimi_k2_mxfp8_stream": 1}.get(w.name, 6)
     keep = cpu_sample_plan(w, ntok) if not args.no_cpu_baseline else []
@@ -287,16 +328,23 @@ def main():
     dominant = max(per, key=per.get)
     log("per-kernel ms: " + ", ".join("%s %.3f" % kv for kv in sorted(per.items(), key=lambda kv: -kv[1])))
 
-    # timed region; the dominant kernel's launches are bracketed by HIP events on its stream
+    # timed region; the dominant kernel's launches are bracketed by HIP events on its stream,
+    # and every step by events of its own (median / min / max over the steps)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with mok.KernelTrace(dominant, capacity=max(16 * args.steps, 8)) as trd:
         start.record()
-        for _ in range(args.steps):
+        evs[0].record()
+        for i in range(args.steps):
             step()
+            evs[i + 1].record()
         end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
+    each = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_stats = {"median": each[len(each) // 2] if len(each) % 2 else 0.5 * (each[len(each) // 2 - 1] + each[len(each) // 2]),
+                  "min": each[0], "max": each[-1]}
     dom = [ms for _, ms in trd.durations_ms()]
     dom_ms = sum(dom) / len(dom)
 
@@ -346,6 +394,8 @@ def main():
         "step_roofline": ({"ms": STEP_ROOFLINE_MS[rkey], "tokens_per_s": w.T / (STEP_ROOFLINE_MS[rkey] * 1e-3),
                            "frac": STEP_ROOFLINE_MS[rkey] / ms_step} if rkey in STEP_ROOFLINE_MS else None),
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "step_ms": {k: round(v, 5) for k, v in step_stats.items()},
+        "hbm_kernels": hbm_kernels(w, per, copy_gbs),
     }
 
     if not args.no_cpu_baseline:
