@@ -250,7 +250,7 @@ def main():
     ap.add_argument("--config", default="kimi_k2_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tile-m", type=int, default=0, help="schedule tile rows (0 = the library's one-wave rule)")
+    ap.add_argument("--tile-m", type=int, default=0, help="schedule tile rows (0 = the library's two-wave rule)")
     ap.add_argument("--fused", action="store_true",
                     help="one persistent launch per pass (bf16, 32-row schedule tiles)")
     ap.add_argument("--replay", action="store_true",

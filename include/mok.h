@@ -128,8 +128,9 @@ typedef enum mok_dtype { MOK_F32 = 0, MOK_BF16 = 1, MOK_MXFP8 = 2, MOK_MXFP4 = 3
  * act = MOK_BF16 (anything else: MOK_ERR_DTYPE); MOK_MXFP4 needs H and I multiples
  * of 256 (else MOK_ERR_SHAPE).
  * tile_m: rows per schedule tile (32, 64 or 128); 0 picks the largest tile
- *   for which the FC1 GEMM has at least one full wave of tiles (one per compute
- *   unit) even if every row went to one expert; 32 with MOK_FLAG_FUSED.
+ *   that still gives every grouped GEMM at least two full waves of the
+ *   GPU's compute units (judged on the FC1 GEMM, as if every row went to one
+ *   expert); 32 with MOK_FLAG_FUSED.
  * grid: workgroups of the persistent GEMM kernels; 0 = one wave of the GPU.
  * Micro-batch streaming (MX only; bf16/fp32 need mb_count <= 1): one step is
  *   mb_count micro-batches of T tokens each, forward in any order and backward in

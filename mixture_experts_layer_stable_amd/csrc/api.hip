@@ -84,19 +84,15 @@ mok_status device_cus(int* out) {
 
 // Schedule tile height. The pages' overlap heuristic asks every expert-grouped
 // GEMM for at least two full waves of the machine (dothoosh.com MoK page,
-// "Technical details of the MoK mechanism"), with their kernel's fixed tile. Here the
-// tile height is free, and on gfx950 the row GEMMs of small batches are bound by
-// re-reading each expert's weight panel once per row tile rather than by occupancy:
-// at 2048 tokens (E = 32, k = 2, I = 512) 64-row tiles (one wave of FC1 tiles) make the
-// step 9 % faster than 32-row tiles (two waves). So we take the tallest tile for which
-// even a fully concentrated routing gives (R / BM) * (2I / 256) >= CUs tiles in the FC1
-// GEMM (one full wave), else the smallest tile. The fused passes are built for 32-row
-// tiles and keep them.
+// "Technical details of the MoK mechanism"); we take the tallest tile for which
+// even a fully concentrated routing gives (R / BM) * (2I / 256) >= 2 * CUs
+// tiles in the FC1 GEMM, else the smallest tile. The fused passes are built for 32-row
+// tiles and always take them.
 int choose_tile_m(int64_t R, int I, int cus, bool fused) {
   if (fused) return 32;
   const int cands[3] = {128, 64, 32};
   for (int bm : cands)
-    if ((R / bm) * (int64_t)(2 * I / 256) >= (int64_t)cus) return bm;
+    if ((R / bm) * (int64_t)(2 * I / 256) >= 2LL * cus) return bm;
   return 32;
 }
 

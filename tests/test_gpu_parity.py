@@ -271,15 +271,16 @@ def test_dw_tile_queues_reset_between_launches(gemm):
 
 
 def test_default_tile_height_rule():
-    """tile_m = 0 takes the tallest of 128/64/32 rows for which the FC1 GEMM has at least one
-    tile per compute unit even with every row packed into full tiles ((R / BM) * (2I / 256)
-    >= CUs); MOK_FLAG_FUSED keeps 32 rows; an explicit tile_m is kept."""
+    """tile_m = 0 takes the tallest of 128/64/32 rows for which the FC1 GEMM has at least two
+    tiles per compute unit even with every row packed into full tiles ((R / BM) * (2I / 256)
+    >= 2 CUs: the pages' two full waves); MOK_FLAG_FUSED keeps 32 rows; an explicit tile_m is
+    kept."""
     from mixture_experts_layer_stable_amd import mok
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def rule(R, I):
         for bm in (128, 64, 32):
-            if (R // bm) * (2 * I // 256) >= cus:
+            if (R // bm) * (2 * I // 256) >= 2 * cus:
                 return bm
         return 32
 
@@ -289,8 +290,8 @@ def test_default_tile_height_rule():
         assert mok.schedule_layout_query(d)["tile_m"] == rule(T * k, I), (T, E, k, H, I)
         assert mok.schedule_layout_query(mok.Desc(T, H, E, k, I, act=mok.BF16, flags=mok.FLAG_FUSED))["tile_m"] == 32
         assert mok.schedule_layout_query(mok.Desc(T, H, E, k, I, act=mok.BF16, tile_m=128))["tile_m"] == 128
-    if cus == 256:  # MI355X: the 2048-token workloads take 64-row tiles, the Kimi-K2 shapes 128
-        assert mok.schedule_layout_query(mok.Desc(2048, 1024, 32, 2, 512, act=mok.BF16))["tile_m"] == 64
+    if cus == 256:  # MI355X: the 2048-token workloads take 32-row tiles, the Kimi-K2 shapes 128
+        assert mok.schedule_layout_query(mok.Desc(2048, 1024, 32, 2, 512, act=mok.BF16))["tile_m"] == 32
         assert mok.schedule_layout_query(mok.Desc(16384, 7168, 384, 8, 2048, act=mok.BF16))["tile_m"] == 128
 
 
