@@ -251,7 +251,9 @@ __device__ __forceinline__ void wait_tiles_behind(int behind) {
 // GEMMs; issuing most of the bytes in the first half gains nothing.
 // ---------------------------------------------------------------------------
 
-template <class Tl, class OA, class OB>
+// TR: accumulate the transposed blocks (MFMA operands swapped: the same products summed
+// over the same k, so the same bits), for the epilogue_bf16 layout below.
+template <class Tl, bool TR = false, class OA, class OB>
 __device__ __forceinline__ void ktile_mma(const OA& oa, const OB& ob, const char* cur, bool more, int nk, char* st,
                                           int wave, f32x16_t (&acc)[Tl::FM][Tl::FN]) {
   constexpr int KS = OA::BK / 16;
@@ -275,7 +277,12 @@ __device__ __forceinline__ void ktile_mma(const OA& oa, const OB& ob, const char
 #pragma unroll
     for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < Tl::FN; ++fn) Mma<bf16>::run(acc[fm][fn], a[c][fm], b[c][fn]);
+      for (int fn = 0; fn < Tl::FN; ++fn) {
+        if constexpr (TR)
+          Mma<bf16>::run(acc[fm][fn], b[c][fn], a[c][fm]);
+        else
+          Mma<bf16>::run(acc[fm][fn], a[c][fm], b[c][fn]);
+      }
   });
 }
 
@@ -334,7 +341,7 @@ struct NoKtHook {
 // hook(kt) runs after K-tile kt's MMAs and refill DMAs are issued. A vector-memory
 // operation it issues only makes the later vmcnt waits cover more (completion is in
 // issue order), never less.
-template <class Tl, int STAGES, int EXTRA, class OA, class OB, class HK = NoKtHook>
+template <class Tl, int STAGES, int EXTRA, bool TR = false, class OA, class OB, class HK = NoKtHook>
 __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, char* smem, int wave, int lane,
                                           f32x16_t (&acc)[Tl::FM][Tl::FN], HK hook = HK{}) {
   static_assert(STAGES == 3, "ring_loop waits are written for 3 stages");
@@ -346,7 +353,7 @@ __device__ __forceinline__ void ring_loop(const OA& oa, const OB& ob, int KT, ch
     if (kt + 1 < KT) wait_vmcnt_extra<NI, EXTRA>(pro); else wait_vmcnt_extra<0, EXTRA>(pro);
     ring_barrier();
     const int nk = kt + STAGES - 1;
-    ktile_mma<Tl>(oa, ob, smem + (kt % STAGES) * SB, nk < KT, nk, smem + (nk % STAGES) * SB, wave, acc);
+    ktile_mma<Tl, TR>(oa, ob, smem + (kt % STAGES) * SB, nk < KT, nk, smem + (nk % STAGES) * SB, wave, acc);
     hook(kt);
   }
   __syncthreads();
@@ -479,48 +486,46 @@ __device__ __forceinline__ void dw_queue_leave(int32_t* line, int members) {
   }
 }
 
-// bf16 epilogue through a per-wave LDS patch: each pair of horizontally adjacent
-// 32x32 accumulator blocks (fn, fn+1) is converted into a 32-row x 64-column bf16
-// patch (row pitch 96 elements = 48 dwords, so the two rows one half-wave writes fall
-// on disjoint banks), then read back so that every store instruction writes 8 whole
-// rows of 128 contiguous bytes (lane: row = 8i + lane/8, 16-byte chunk lane%8).
-// Accumulator registers r, r+1 (r even) of a lane hold rows rho, rho+1 of its column;
-// converting them as one packed pair and swapping halves with the neighbouring lane
-// (DPP quad_perm [1,0,3,2] + v_perm_b32) gives the even lane (rho, c..c+1) and the odd
-// lane (rho+1, c-1..c) as whole dwords: three VALU ops and one 4-byte LDS write per
-// two values. FM*FN*2 global stores per lane, as store(row, col, v) with v the 8 bf16
-// at tile (row, col .. col+7). The patch (kBf16PatchBytes) lies outside any ring
-// stage still in use; a wave's LDS operations run in issue order.
-constexpr int kBf16PatchLd = 96;
-constexpr int kBf16PatchBytes = 32 * kBf16PatchLd * 2;
+// bf16 epilogue through a per-wave LDS patch, from transposed accumulator blocks
+// (ktile_mma with TR): a lane holds 16 column values of one tile row, lane%32 being the
+// row and registers 4g..4g+3 the columns 8g + 4(lane/32) .. +3. One conversion packs two
+// neighbouring columns, and four columns go into the 32-row x 64-column patch of a block
+// pair in one 8-byte write; with a row pitch of 34 dwords the 32 rows that a half-wave
+// writes fall on distinct bank pairs. The patch is read back (two 8-byte reads: odd rows
+// start 8-byte aligned) so that every store instruction writes 8 whole rows of 128
+// contiguous bytes (lane: row = 8i + lane/8, 16-byte chunk lane%8). FM*FN*2 global
+// stores per lane, as store(row, col, v) with v the 8 bf16 at tile (row, col .. col+7).
+// The patch (kBf16PatchBytes) lies outside any ring stage still in use; a wave's LDS
+// operations run in issue order.
+constexpr int kBf16PatchPitch = 34;  // dwords
+constexpr int kBf16PatchBytes = 32 * kBf16PatchPitch * 4;
 
 template <class Tl, class F>
 __device__ __forceinline__ void epilogue_bf16(f32x16_t (&acc)[Tl::FM][Tl::FN], char* patch, int wm, int wn, int lane,
                                               F&& store) {
   static_assert(Tl::FN % 2 == 0, "blocks are stored in horizontal pairs");
-  constexpr int PLD = kBf16PatchLd;
-  const int odd = lane & 1;
-  const uint32_t sel = odd ? 0x07060302u : 0x01000504u;
-  const int cpair = (lane & 31) & ~1;
+  constexpr int P = kBf16PatchPitch;
+  const int m = lane & 31, h = lane >> 5;
+  uint32_t* pw = reinterpret_cast<uint32_t*>(patch);
 #pragma unroll
   for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Tl::FN; fn += 2) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + odd;
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const uint32_t p = bf16x2_rne(acc[fm][fn + hb][r], acc[fm][fn + hb][r + 1]);
-          const uint32_t q = __builtin_amdgcn_mov_dpp(p, 0xB1, 0xF, 0xF, true);
-          *reinterpret_cast<uint32_t*>(patch + (row * PLD + 32 * hb + cpair) * 2) = __builtin_amdgcn_perm(p, q, sel);
+        for (int g = 0; g < 4; ++g) {
+          uint2 v;
+          v.x = bf16x2_rne(acc[fm][fn + hb][4 * g], acc[fm][fn + hb][4 * g + 1]);
+          v.y = bf16x2_rne(acc[fm][fn + hb][4 * g + 2], acc[fm][fn + hb][4 * g + 3]);
+          *reinterpret_cast<uint2*>(pw + m * P + 16 * hb + 4 * g + 2 * h) = v;
         }
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * i + (lane >> 3), c = (lane & 7) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(patch + (row * PLD + c) * 2);
-        store(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c, v);
+        const uint2 lo = *reinterpret_cast<const uint2*>(pw + row * P + c / 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(pw + row * P + c / 2 + 2);
+        store(wm * Tl::WTM + fm * 32 + row, wn * Tl::WTN + fn * 32 + c, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     }
 }

@@ -331,9 +331,9 @@ __global__ __launch_bounds__(Tl::NT) void dw_gemm2_pipe_kernel(DwArgs2 a, int E)
     };
     if (Q && KT == 0 && tid == 0) claim = dw_queue_claim(qline);
     if (first)
-      ring_loop<Tl, STAGES, 0>(oa, ob, KT, smem, wave, lane, acc, hook);
+      ring_loop<Tl, STAGES, 0, true>(oa, ob, KT, smem, wave, lane, acc, hook);
     else
-      ring_loop<Tl, STAGES, EXTRA>(oa, ob, KT, smem, wave, lane, acc, hook);
+      ring_loop<Tl, STAGES, EXTRA, true>(oa, ob, KT, smem, wave, lane, acc, hook);
     bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
     int64_t Ln;
     if constexpr (Q) {

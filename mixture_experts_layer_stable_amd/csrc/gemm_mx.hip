@@ -92,7 +92,8 @@ __device__ __forceinline__ v8i32_t join8(const uint4& lo, const uint4& hi) {
 // One 64-k step of the K-tile in `cur`. E4M3: 32 bytes per lane (frag positions 2KS,
 // 2KS+1), opsel = byte 2*KS of scale dword 0. E2M1: 16 bytes per lane (frag position KS;
 // the instruction reads the low 4 dwords), opsel = byte 2*(KS%2) of scale dword KS/2.
-template <int F, int KS, class Tl, class OA, class OB>
+// TR: operands (and their scales) swapped, giving transposed blocks with the same bits.
+template <int F, int KS, bool TR, class Tl, class OA, class OB>
 __device__ __forceinline__ void mx_kstep(const OA& oa, const OB& ob, const char* ca, const char* cb,
                                          const uint32_t (&xa)[MxFmt<F>::SD][Tl::FM],
                                          const uint32_t (&xb)[MxFmt<F>::SD][Tl::FN], f32x16_t (&acc)[Tl::FM][Tl::FN]) {
@@ -110,8 +111,12 @@ __device__ __forceinline__ void mx_kstep(const OA& oa, const OB& ob, const char*
   for (int fm = 0; fm < Tl::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Tl::FN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fm], b[fn], acc[fm][fn], FMT, FMT, OP,
-                                                                    (int)xa[D][fm], OP, (int)xb[D][fn]);
+      if constexpr (TR)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[fn], a[fm], acc[fm][fn], FMT, FMT, OP,
+                                                                      (int)xb[D][fn], OP, (int)xa[D][fm]);
+      else
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fm], b[fn], acc[fm][fn], FMT, FMT, OP,
+                                                                      (int)xa[D][fm], OP, (int)xb[D][fn]);
 }
 
 // STAGES-deep ring as in the bf16 core; a stage holds A rows, B rows, A scales, B scales.
@@ -137,7 +142,8 @@ __device__ __forceinline__ void mx_ring_prologue(const OA& oa, const OB& ob, con
 }
 
 // hook(kt) runs after K-tile kt's MMAs and refill DMAs are issued (as in ring_loop).
-template <int F, class Tl, int STAGES, int EXTRA, class OA, class OB, class SA, class SB, class HK = NoKtHook>
+template <int F, class Tl, int STAGES, int EXTRA, bool TR = false, class OA, class OB, class SA, class SB,
+          class HK = NoKtHook>
 __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const SA& sa, const SB& sb, int KT,
                                              char* smem, int wave, int lane, f32x16_t (&acc)[Tl::FM][Tl::FN],
                                              HK hook = HK{}) {
@@ -169,15 +175,15 @@ __device__ __forceinline__ void mx_ring_loop(const OA& oa, const OB& ob, const S
 #pragma unroll
       for (int fn = 0; fn < Tl::FN; ++fn) xb[d][fn] = sb.get(cur + OFF_SB, fn, lane, d);
     }
-    mx_kstep<F, 0, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+    mx_kstep<F, 0, TR, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
     if constexpr (F == 0) {
       if (nk < KT) ob.issue(nk, st + OFF_B, wave);
-      mx_kstep<F, 1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      mx_kstep<F, 1, TR, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
     } else {
-      mx_kstep<F, 1, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      mx_kstep<F, 1, TR, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
       if (nk < KT) ob.issue(nk, st + OFF_B, wave);
-      mx_kstep<F, 2, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
-      mx_kstep<F, 3, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      mx_kstep<F, 2, TR, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
+      mx_kstep<F, 3, TR, Tl>(oa, ob, cur, cur + OFF_B, xa, xb, acc);
     }
     hook(kt);
   }
@@ -485,9 +491,9 @@ __global__ __launch_bounds__(Tl::NT) void dw_mx_pipe_kernel(MxDwArgs a, int E) {
     };
     if (Q && KT == 0 && tid == 0) claim = dw_queue_claim(qline);
     if (first)
-      mx_ring_loop<F, Tl, STAGES, 0>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
+      mx_ring_loop<F, Tl, STAGES, 0, true>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
     else
-      mx_ring_loop<F, Tl, STAGES, EXTRA>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
+      mx_ring_loop<F, Tl, STAGES, EXTRA, true>(oa, ob, sa, sb, KT, smem, wave, lane, acc, hook);
     bf16* out = reinterpret_cast<bf16*>(a.out) + ((int64_t)e * a.M + mt * Tl::BM) * a.N + nt * Tl::BN;
     int64_t Ln;
     if constexpr (Q) {
