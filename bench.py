@@ -125,7 +125,8 @@ def kernel_work(w, name, active_experts=None):
     if name in flops:
         return "mfma", flops[name]
     nbytes = {"combine": R * H * es + T * H * es + 4 * R,
-              "dx_reduce": R * H * es + T * H * es + 8 * R + R * H * es,
+              # each slot's router-weight row is read from cache: Wr counts once
+              "dx_reduce": R * H * es + T * H * es + 8 * R + E * H * es,
               # bf16: dWr also writes the routed-order x rows that dW1 reads
               "dwr": R * H * es + E * H * es + 8 * R + (R * H * es if w.act == "bf16" else 0),
               "gather": 2 * R * H * es + 8 * R,  # routed-order dO = g*dY rows for dW2
