@@ -262,8 +262,8 @@ def main():
                     help="first run one plain 1 GiB device-to-device copy (known bytes, for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU's share of the layer step; multi-GPU runs (--gpus %d) are not part of "
-              "this build" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer step; the library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
