@@ -89,7 +89,11 @@ struct ColQuantArgs {
 
 template <int FM>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
-  __shared__ float tile[128][65];
+  // The 128-row x 64-feature tile as raw bf16 (16.5 KB, so eight workgroups share a CU),
+  // row pitch 66 elements (33 dwords): with rows 64..127 rotated by 16 columns, the column
+  // reads of a wave below fall on distinct banks.
+  constexpr int TP = 66;
+  __shared__ __align__(16) uint16_t tile[128 * TP];
   const int r0 = blockIdx.x * 128, f0 = blockIdx.y * 64, z = blockIdx.z;
   if (guard_fail(a.guard) || (a.kdev != nullptr && r0 >= *a.kdev)) return;
   const bf16* src = a.src + (int64_t)z * a.src_mat;
@@ -99,23 +103,21 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
     const int row = v >> 3, c8 = (v & 7) * 8;
     const int r = r0 + row;
     const int64_t p = a.rowmap != nullptr ? (int64_t)a.rowmap[r] : (int64_t)r;
-    float f[8];
-    if (p >= 0) {
-      unpack(ldg16(src + p * a.ld + f0 + c8), f, (bf16*)nullptr);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) f[q] = 0.0f;
-    }
+    const uint4 raw = p >= 0 ? ldg16(src + p * a.ld + f0 + c8) : make_uint4(0u, 0u, 0u, 0u);
     const int pc = (c8 + 16 * ((row >> 6) & 1)) & 63;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) tile[row][pc + q] = f[q];
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + row * TP + pc);
+    t32[0] = raw.x;
+    t32[1] = raw.y;
+    t32[2] = raw.z;
+    t32[3] = raw.w;
   }
+  const auto at = [&](int row, int col) { return __uint_as_float((uint32_t)tile[row * TP + col] << 16); };
   __syncthreads();
   const int f = 16 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 2), b = threadIdx.x & 3;
   const int pf = (f + 16 * (b >> 1)) & 63;  // rows 32b .. 32b+31 all carry the same rotation
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * b + i][pf]));
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(at(32 * b + i, pf)));
   const int64_t orow = (int64_t)z * a.F + f0 + f;
   uint32_t sb;
   if constexpr (FM == 0) {
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = 32 * b + 4 * j;
-      w[j] = mx_pack4(tile[i][pf], tile[i + 1][pf], tile[i + 2][pf], tile[i + 3][pf], inv);
+      w[j] = mx_pack4(at(i, pf), at(i + 1, pf), at(i + 2, pf), at(i + 3, pf), inv);
     }
     uint8_t* qo = a.q + orow * a.out_ld + r0 + 32 * b;
     stg16(qo, make_uint4(w[0], w[1], w[2], w[3]));
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(ColQuantArgs a) {
     const float inv = mx_inv_scale(sb);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_code(tile[32 * b + i][pf] * inv) << (4 * (i & 7));
+    for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_code(at(32 * b + i, pf) * inv) << (4 * (i & 7));
     stg16(a.q + orow * (a.out_ld / 2) + (r0 + 32 * b) / 2, make_uint4(w[0], w[1], w[2], w[3]));
   }
   const int64_t kb = r0 / 32 + b;
