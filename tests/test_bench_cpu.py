@@ -68,3 +68,17 @@ def test_traffic_figure_only_for_the_measured_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("dw2", "demo") is None  # no summary for that kernel
     (csrc / "k.hip").write_text("// kernel v2\n")
     assert bench.measured_traffic("dw1", "demo") is None  # sources changed since the counters
+
+
+def test_bandwidth_kernels_count_compulsory_bytes():
+    """The elementwise kernels' algorithmic bytes at the Kimi-K2 shape (bf16, R = T*k routed
+    rows): combine reads the R partial rows and writes the T output rows; dX reduce does the
+    same plus the router-weight matrix once (each slot's Wr row comes from cache) and the
+    dz/idx words; dWr reads the routed x rows and also writes them in routed order for dW1;
+    the dO gather reads the routed dY rows and writes g*dY in routed order."""
+    w = inputs.WORKLOADS["kimi_k2_bf16"]
+    T, R, H, E = w.T, w.T * w.k, w.H, w.E
+    assert bench.kernel_work(w, "combine") == ("hbm", 2 * R * H + 2 * T * H + 4 * R)
+    assert bench.kernel_work(w, "dx_reduce") == ("hbm", 2 * R * H + 2 * T * H + 8 * R + 2 * E * H)
+    assert bench.kernel_work(w, "dwr") == ("hbm", 2 * R * H + 2 * E * H + 8 * R + 2 * R * H)
+    assert bench.kernel_work(w, "gather") == ("hbm", 4 * R * H + 8 * R)
